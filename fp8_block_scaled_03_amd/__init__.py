@@ -1,0 +1,12 @@
+"""FP8 block-scaled linear-layer path for AMD Instinct MI355X (gfx950).
+
+Quantizers (BF16 -> E4M3 codes + FP32 scales: 1x128 row tiles, 128x128
+weight blocks, token-axis tiles) and block-scaled FP8 GEMMs (fprop, dgrad,
+wgrad) in hand-written HIP kernels behind the C ABI of include/fp8bs.h.  The
+Python functions here carry the C names and only marshal arguments.
+"""
+from ._binding import (FP8BS_OUT_BF16, FP8BS_OUT_F32, Fp8bsError, capi,  # noqa: F401
+                       fp8_encode_e4m3, fp8_gemm_dgrad, fp8_gemm_fprop, fp8_gemm_wgrad,
+                       fp8_gemm_wgrad_workspace_bytes, fp8_quantize_block,
+                       fp8_quantize_rowtile, fp8_quantize_transposed, fp8bs_status_string,
+                       fp8bs_version)

@@ -93,12 +93,11 @@ class Config:
 
 def _c5_gemms(T: int):
     g = []
-    lin = (("qkv", QKV_WIDTH, HIDDEN, "X_qkv", "dY_qkv"),
-           ("o", HIDDEN, HIDDEN, "X_o", "dY_o"),
-           ("gu", 2 * FFN, HIDDEN, "X_mlp", "dY_gu"),
-           ("down", HIDDEN, FFN, "H", "dY_d"))
-    for nm, n_out, k_in, x, dy in lin:
-        w = "W_" + nm
+    lin = (("qkv", QKV_WIDTH, HIDDEN, "X_qkv", "dY_qkv", "W_qkv"),
+           ("o", HIDDEN, HIDDEN, "X_o", "dY_o", "W_o"),
+           ("gu", 2 * FFN, HIDDEN, "X_mlp", "dY_gu", "W_gu"),
+           ("down", HIDDEN, FFN, "H", "dY_d", "W_d"))
+    for nm, n_out, k_in, x, dy, w in lin:
         # fprop: Y[T, n_out] = X[T, k_in] W[n_out, k_in]^T
         g.append(Gemm(f"{nm}.fprop", "fprop", x, w, T, n_out, k_in, "bf16"))
         # dgrad: dX[T, k_in] = dY[T, n_out] W[n_out, k_in]

@@ -1,0 +1,178 @@
+/*
+ * fp8bs.h -- C ABI of libfp8bs: FP8 (E4M3) block-scaled quantizers and GEMMs
+ * for the main linear layers of a decoder, on AMD Instinct MI355X (gfx950).
+ *
+ * The method: the Puro-2B technical report (lkr-homepage blog, section 2
+ * "FP8") runs the matmuls of the main linear layers in FP8 using DeepSeek-V3's
+ * fine-grained block quantization, and keeps numerically sensitive operations
+ * and training state in BF16 or FP32.  This library implements that path with
+ * the following reading of the passage:
+ *   - codes are OCP E4M3FN (bias 7, no infinities, largest finite 448);
+ *   - activations and gradients are quantized in 1x128 tiles along the
+ *     contraction axis, weights in 128x128 blocks, one FP32 scale per tile;
+ *   - per tile: a = max(amax, 2^-100); s = a/448 and inv = 448/a, each one
+ *     correctly rounded FP32 division; code = E4M3 round-to-nearest-even of
+ *     clamp(fl32(x*inv), -448, 448); x is represented by dec(code)*s;
+ *   - each GEMM sums, per 128-wide contraction block, the FP8 products in
+ *     FP32 and folds that partial sum into an FP32 accumulator multiplied by
+ *     the two operands' scales for the block.  Outputs are BF16 or FP32.
+ *
+ * Conventions shared by every call:
+ *   - Every tensor pointer is a device pointer on the current HIP device,
+ *     row-major and contiguous.  BF16 is passed as raw uint16_t bit patterns,
+ *     E4M3 codes as uint8_t.
+ *   - Ownership: the caller owns every buffer.  The library allocates nothing,
+ *     frees nothing and keeps no pointer after a call returns.
+ *   - Streams: work is enqueued on `stream` (NULL = the null stream) and the
+ *     call returns without waiting.  Outputs are valid once the stream has
+ *     reached the call.
+ *   - Errors: argument errors are detected before anything is enqueued; the
+ *     call then returns the status and leaves every output untouched.  A
+ *     failed launch returns FP8BS_ERR_HIP.  Faults inside a kernel surface at
+ *     the caller's next synchronization of the stream.  Inputs must be finite;
+ *     the library does not check this (a non-finite input gives unspecified
+ *     codes for its tile).
+ *   - Alignment: code and BF16 pointers must be 16-byte aligned, scale and
+ *     FP32 pointers 4-byte aligned (FP8BS_ERR_ALIGN otherwise).
+ *   - Empty tensors (a zero dimension) are valid; their pointers may be NULL.
+ *   - Threads: calls are re-entrant and may be made from several host threads
+ *     as long as their output buffers do not overlap.
+ */
+#ifndef FP8BS_H
+#define FP8BS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* A hipStream_t, spelled without the HIP headers. */
+typedef struct ihipStream_t* fp8bs_stream_t;
+
+typedef enum {
+    FP8BS_OK = 0,
+    FP8BS_ERR_NULL = 1,        /* a required pointer is NULL */
+    FP8BS_ERR_SHAPE = 2,       /* a dimension is negative, or not a multiple of 128 where required */
+    FP8BS_ERR_ALIGN = 3,       /* a pointer is not aligned as required */
+    FP8BS_ERR_DTYPE = 4,       /* unknown output dtype */
+    FP8BS_ERR_WORKSPACE = 5,   /* workspace given but too small */
+    FP8BS_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed */
+    FP8BS_ERR_UNSUPPORTED = 7  /* the device is not gfx950 */
+} fp8bs_status;
+
+typedef enum {
+    FP8BS_OUT_F32 = 0,
+    FP8BS_OUT_BF16 = 1         /* round to nearest, ties to even */
+} fp8bs_out_dtype;
+
+/*
+ * Row-tile quantizer (activations for fprop, gradients for dgrad).
+ * Puro-2B report, section 2 "FP8": fine-grained quantization of the FP8
+ * matmul operands; 1x128 tiles along the contraction axis.
+ *   x  bf16 [M, K]  input
+ *   q  u8   [M, K]  E4M3 codes (output)
+ *   s  f32  [M, K/128]  s[r][j] is the scale of x[r][128j .. 128j+127] (output)
+ * M >= 0 (any value), K >= 0 and a multiple of 128.
+ */
+fp8bs_status fp8_quantize_rowtile(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s,
+                                  fp8bs_stream_t stream);
+
+/*
+ * Block quantizer (weights).
+ * Puro-2B report, section 2 "FP8": block quantization of the weight operand;
+ * 128x128 blocks.
+ *   w    bf16 [N, K]  input
+ *   q    u8   [N, K]  E4M3 codes (output)
+ *   q_t  u8   [K, N]  the same codes transposed, q_t[k][n] == q[n][k]
+ *                     (output; may be NULL when dgrad is not needed)
+ *   s    f32  [N/128, K/128]  s[i][j] covers rows 128i.. and columns 128j..
+ * N, K >= 0 and multiples of 128.
+ */
+fp8bs_status fp8_quantize_block(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, uint8_t* q_t,
+                                float* s, fp8bs_stream_t stream);
+
+/*
+ * Token-axis (transposed) quantizer for the weight-gradient operands.
+ * The weight gradient contracts over tokens, so its operands are quantized in
+ * 1x128 tiles of 128 consecutive tokens of one channel: the row-tile
+ * quantizer applied to x transposed (Puro-2B report, section 2 "FP8", read
+ * for the weight-gradient matmul).
+ *   x   bf16 [M, C]  input (M tokens, C channels)
+ *   qt  u8   [C, M]  codes of x transposed (output)
+ *   st  f32  [C, M/128]  st[c][b] is the scale of x[128b .. 128b+127][c] (output)
+ * M >= 0 and a multiple of 128; C >= 0 and a multiple of 128.
+ */
+fp8bs_status fp8_quantize_transposed(const uint16_t* x, int64_t M, int64_t C, uint8_t* qt,
+                                     float* st, fp8bs_stream_t stream);
+
+/*
+ * fprop GEMM: Y = X W^T (Puro-2B report, section 2 "FP8": the forward matmul
+ * of a main linear layer in FP8).
+ *   xq  u8  [M, K],  xs f32 [M, K/128]          from fp8_quantize_rowtile(X)
+ *   wq  u8  [N, K],  ws f32 [N/128, K/128]      from fp8_quantize_block(W)
+ *   y   [M, N] of dtype yt (FP32 or BF16)       output
+ * y[m][n] = sum_kb xs[m][kb] * ws[n/128][kb] * sum_{k in kb} dec(xq[m][k]) dec(wq[n][k]).
+ * M >= 0 (any value); N, K >= 0 and multiples of 128.  K == 0 writes zeros.
+ */
+fp8bs_status fp8_gemm_fprop(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                            void* y, fp8bs_out_dtype yt, int64_t M, int64_t N, int64_t K,
+                            fp8bs_stream_t stream);
+
+/*
+ * dgrad GEMM: dX = dY W (Puro-2B report, section 2 "FP8": the input-gradient
+ * matmul of a main linear layer in FP8).  W keeps the quantization of the
+ * forward pass; its codes are read in the transposed copy.
+ *   dyq  u8 [M, N],  dys f32 [M, N/128]         from fp8_quantize_rowtile(dY)
+ *   wq_t u8 [K, N],  ws  f32 [N/128, K/128]     q_t and s of fp8_quantize_block(W[N,K])
+ *   dx   [M, K] of dtype dxt                    output
+ * dx[m][k] = sum_nb dys[m][nb] * ws[nb][k/128] * sum_{n in nb} dec(dyq[m][n]) dec(wq_t[k][n]).
+ * M >= 0 (any value); N, K >= 0 and multiples of 128.  N == 0 writes zeros.
+ */
+fp8bs_status fp8_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wq_t,
+                            const float* ws, void* dx, fp8bs_out_dtype dxt, int64_t M, int64_t N,
+                            int64_t K, fp8bs_stream_t stream);
+
+/*
+ * wgrad GEMM: dW = dY^T X, contracted over M tokens (Puro-2B report, section
+ * 2 "FP8": the weight-gradient matmul of a main linear layer in FP8).
+ *   dytq u8 [N, M],  dyts f32 [N, M/128]        from fp8_quantize_transposed(dY[M,N])
+ *   xtq  u8 [K, M],  xts  f32 [K, M/128]        from fp8_quantize_transposed(X[M,K])
+ *   dw   f32 [N, K]                             output
+ * dw[n][k] = sum_mb dyts[n][mb] * xts[k][mb] * sum_{m in mb} dec(dytq[n][m]) dec(xtq[k][m]).
+ * M, N, K >= 0 and multiples of 128.  M == 0 writes zeros.
+ * workspace: optional device scratch for splitting the contraction across
+ * workgroups (see fp8_gemm_wgrad_workspace_bytes).  With workspace == NULL or
+ * workspace_bytes == 0 the call does not split.  A non-NULL workspace smaller
+ * than the query returns FP8BS_ERR_WORKSPACE.  The split result is summed in
+ * a fixed order, so it is deterministic run to run.
+ */
+fp8bs_status fp8_gemm_wgrad(const uint8_t* dytq, const float* dyts, const uint8_t* xtq,
+                            const float* xts, float* dw, int64_t M, int64_t N, int64_t K,
+                            void* workspace, size_t workspace_bytes, fp8bs_stream_t stream);
+
+/* Bytes of workspace fp8_gemm_wgrad uses for this shape on the current
+ * device (16-byte aligned); 0 when it would not split.  Negative or invalid
+ * shapes give 0. */
+size_t fp8_gemm_wgrad_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * Diagnostic: the quantizers' FP32 -> E4M3 step on its own, elementwise:
+ * q[i] = E4M3 round-to-nearest-even of clamp(x[i], -448, 448).  Lets a test
+ * sweep the device conversion over any set of FP32 values.
+ *   x f32 [n] (16-byte aligned), q u8 [n] (16-byte aligned); n >= 0.
+ */
+fp8bs_status fp8_encode_e4m3(const float* x, int64_t n, uint8_t* q, fp8bs_stream_t stream);
+
+/* Static string naming a status (never NULL). */
+const char* fp8bs_status_string(fp8bs_status status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int fp8bs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BS_H */

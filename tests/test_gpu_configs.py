@@ -1,0 +1,92 @@
+"""GPU parity at the full Qwen3-1.7B-like configurations, launched exactly as
+the benchmark launches them, compared with the oracle on sampled output rows
+(row tiles and weight blocks are local, so the oracle quantizes only what the
+sampled rows need).  Quantizer outputs of these tensors are compared in full
+by test_gpu_quant."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp8_block_scaled_03_amd as fp8
+from fp8_block_scaled_03_amd import inputs
+from helpers import check_bf16, check_f32, to_dev_bf16, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def sample_rows(n, k=48, seed=0):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, n - 1], rng.choice(n, size=min(k, n), replace=False)]))
+
+
+def gemm_case(kind, abits, bbits, out, rows, dev_cache=None):
+    """Run one GEMM of a configuration on the GPU (full size) and the oracle
+    on the sampled rows.  abits is the row-side operand [M, .] for fprop /
+    dgrad and dY [M, N] for wgrad (rows then index dW's rows = dY channels)."""
+    a, b = to_dev_bf16(abits), to_dev_bf16(bbits)
+    if kind == "fprop":
+        aq, as_ = fp8.fp8_quantize_rowtile(a)
+        bq, _, bs = fp8.fp8_quantize_block(b, with_transpose=False)
+        y = fp8.fp8_gemm_fprop(aq, as_, bq, bs, out_dtype=out)
+        torch.cuda.synchronize()
+        got = to_np(y)[rows]
+        oq, os_ = oracle.quantize_rowtile(abits[rows])
+        wq, _, ws = oracle.quantize_block(bbits, with_transpose=False)
+        ref = oracle.gemm_fprop(oq, os_, wq, ws)
+        ad, bd = oracle.dequantize_rows(oq, os_), oracle.dequantize_block(wq, ws)
+    elif kind == "dgrad":
+        aq, as_ = fp8.fp8_quantize_rowtile(a)
+        _, bqt, bs = fp8.fp8_quantize_block(b)
+        y = fp8.fp8_gemm_dgrad(aq, as_, bqt, bs, out_dtype=out)
+        torch.cuda.synchronize()
+        got = to_np(y)[rows]
+        oq, os_ = oracle.quantize_rowtile(abits[rows])
+        wq, wqt, ws = oracle.quantize_block(bbits)
+        ref = oracle.gemm_dgrad(oq, os_, wqt, ws)
+        ad, bd = oracle.dequantize_rows(oq, os_), oracle.dequantize_block(wq, ws).T
+    else:
+        atq, ats = fp8.fp8_quantize_transposed(a)
+        btq, bts = fp8.fp8_quantize_transposed(b)
+        y = fp8.fp8_gemm_wgrad(atq, ats, btq, bts, workspace="auto")
+        torch.cuda.synchronize()
+        got = to_np(y)[rows]
+        oq, os_ = oracle.quantize_transposed(np.ascontiguousarray(abits[:, rows]))
+        xq, xs = oracle.quantize_transposed(bbits)
+        ref = oracle.gemm_wgrad(oq, os_, xq, xs)
+        ad, bd = oracle.dequantize_rows(oq, os_), oracle.dequantize_rows(xq, xs)
+    if out == "f32":
+        check_f32(got, ref, ad, bd, kind)
+    else:
+        check_bf16(got, ref, ad, bd, kind)
+
+
+@pytest.mark.parametrize("cfg", ["tiny", "qkv", "mlp", "down_bwd"])
+def test_config_gemms_sampled(cfg):
+    c = inputs.CONFIGS[cfg]
+    for g in c.gemms:
+        _say(f"config {cfg} {g.name} M={g.M} N={g.N} K={g.K} out={g.out}")
+        abits = inputs.tensor(cfg, g.a)
+        bbits = inputs.tensor(cfg, g.b)
+        n_rows = g.M if g.kind != "wgrad" else g.N
+        rows = np.arange(n_rows) if cfg == "tiny" else sample_rows(n_rows, seed=c.key)
+        gemm_case(g.kind, abits, bbits, g.out, rows)
+
+
+@pytest.mark.parametrize("layer", [0, 27])
+def test_linear_set_layer_sampled(layer):
+    """One layer of the 28-layer, 16,384-token linear set: all 12 GEMMs."""
+    c = inputs.CONFIGS["linear_set"]
+    cache = {}
+    for g in c.gemms:
+        _say(f"linear_set layer {layer} {g.name} M={g.M} N={g.N} K={g.K}")
+        for nm in (g.a, g.b):
+            if nm not in cache:
+                cache[nm] = inputs.tensor("linear_set", nm, layer=layer)
+        n_rows = g.M if g.kind != "wgrad" else g.N
+        rows = sample_rows(n_rows, k=16, seed=layer)
+        gemm_case(g.kind, cache[g.a], cache[g.b], g.out, rows)

@@ -1,0 +1,198 @@
+"""GPU parity of the block-scaled FP8 GEMMs (fprop, dgrad, wgrad), through
+the C ABI, against the CPU oracle applied to the oracle's own quantization of
+the same seeded inputs.  FP32 outputs: relF <= 1e-5 and |err| <= 1e-4 ||a_i||
+||b_j||.  BF16 outputs: within one BF16 ulp of bf16_RNE(oracle)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp8_block_scaled_03_amd as fp8
+from fp8_block_scaled_03_amd import inputs
+from helpers import check_bf16, check_f32, to_dev_bf16, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def run_fprop(xbits, wbits, out):
+    x, w = to_dev_bf16(xbits), to_dev_bf16(wbits)
+    xq, xs = fp8.fp8_quantize_rowtile(x)
+    wq, _, ws = fp8.fp8_quantize_block(w, with_transpose=False)
+    y = fp8.fp8_gemm_fprop(xq, xs, wq, ws, out_dtype=out)
+    torch.cuda.synchronize()
+    return to_np(y)
+
+
+def ref_fprop(xbits, wbits, rows=None):
+    xq, xs = oracle.quantize_rowtile(xbits if rows is None else xbits[rows])
+    wq, _, ws = oracle.quantize_block(wbits, with_transpose=False)
+    y = oracle.gemm_fprop(xq, xs, wq, ws)
+    return y, oracle.dequantize_rows(xq, xs), oracle.dequantize_block(wq, ws)
+
+
+def run_dgrad(dybits, wbits, out):
+    dy, w = to_dev_bf16(dybits), to_dev_bf16(wbits)
+    dyq, dys = fp8.fp8_quantize_rowtile(dy)
+    _, wqt, ws = fp8.fp8_quantize_block(w)
+    dx = fp8.fp8_gemm_dgrad(dyq, dys, wqt, ws, out_dtype=out)
+    torch.cuda.synchronize()
+    return to_np(dx)
+
+
+def ref_dgrad(dybits, wbits, rows=None):
+    dyq, dys = oracle.quantize_rowtile(dybits if rows is None else dybits[rows])
+    wq, wqt, ws = oracle.quantize_block(wbits)
+    dx = oracle.gemm_dgrad(dyq, dys, wqt, ws)
+    return dx, oracle.dequantize_rows(dyq, dys), oracle.dequantize_block(wq, ws).T
+
+
+def run_wgrad(dybits, xbits, workspace=None):
+    dy, x = to_dev_bf16(dybits), to_dev_bf16(xbits)
+    dytq, dyts = fp8.fp8_quantize_transposed(dy)
+    xtq, xts = fp8.fp8_quantize_transposed(x)
+    dw = fp8.fp8_gemm_wgrad(dytq, dyts, xtq, xts, workspace=workspace)
+    torch.cuda.synchronize()
+    return to_np(dw)
+
+
+def ref_wgrad(dybits, xbits, rows=None):
+    dyc = dybits if rows is None else np.ascontiguousarray(dybits[:, rows])
+    dytq, dyts = oracle.quantize_transposed(dyc)
+    xtq, xts = oracle.quantize_transposed(xbits)
+    dw = oracle.gemm_wgrad(dytq, dyts, xtq, xts)
+    return dw, oracle.dequantize_rows(dytq, dyts), oracle.dequantize_rows(xtq, xts)
+
+
+FPROP_CASES = [  # (M, N, K) -- ragged M, several tiles in every direction
+    (256, 256, 512),
+    (1000, 384, 640),
+    (77, 128, 128),
+    (513, 512, 1024),
+]
+
+
+@pytest.mark.parametrize("M,N,K", FPROP_CASES)
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_fprop_parity(M, N, K, out):
+    _say(f"fprop {M}x{N}x{K} {out}")
+    xb = inputs.random_bits((20, M, K), (M, K), "wide")
+    wb = inputs.bf16_bits(oracle.bf16_to_f32(inputs.random_bits((21, N, K), (N, K))) * np.float32(0.02))
+    y = run_fprop(xb, wb, out)
+    ref, a, b = ref_fprop(xb, wb)
+    if out == "f32":
+        check_f32(y, ref, a, b, "fprop")
+    else:
+        check_bf16(y, ref, a, b, "fprop bf16")
+
+
+DGRAD_CASES = [(256, 256, 512), (300, 640, 384), (1, 128, 256)]
+
+
+@pytest.mark.parametrize("M,N,K", DGRAD_CASES)
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_dgrad_parity(M, N, K, out):
+    _say(f"dgrad {M}x{N}x{K} {out}")
+    dyb = inputs.student_t((22, M, N), (M, N), 3.0, 1e-3)
+    wb = inputs.normal((23, N, K), (N, K), 0.02)
+    dx = run_dgrad(dyb, wb, out)
+    ref, a, b = ref_dgrad(dyb, wb)
+    if out == "f32":
+        check_f32(dx, ref, a, b, "dgrad")
+    else:
+        check_bf16(dx, ref, a, b, "dgrad bf16")
+
+
+WGRAD_CASES = [(256, 256, 384), (1024, 384, 256), (128, 128, 128), (2048, 512, 640)]
+
+
+@pytest.mark.parametrize("M,N,K", WGRAD_CASES)
+def test_wgrad_parity(M, N, K):
+    _say(f"wgrad {M}x{N}x{K}")
+    dyb = inputs.student_t((24, M, N), (M, N), 3.0, 1e-3)
+    xb = inputs.random_bits((25, M, K), (M, K), "wide")
+    dw = run_wgrad(dyb, xb)
+    ref, a, b = ref_wgrad(dyb, xb)
+    check_f32(dw, ref, a, b, "wgrad")
+
+
+def test_wgrad_split_matches_unsplit_bitwise_and_oracle():
+    M, N, K = 8192, 256, 256          # long contraction, few tiles: the split case
+    dyb = inputs.student_t((26, M, N), (M, N), 3.0, 1e-3)
+    xb = inputs.normal((27, M, K), (M, K))
+    ws_bytes = fp8.fp8_gemm_wgrad_workspace_bytes(M, N, K)
+    _say(f"wgrad workspace bytes {ws_bytes}")
+    a = run_wgrad(dyb, xb, workspace="auto")
+    b = run_wgrad(dyb, xb, workspace="auto")
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), "split result not deterministic"
+    ref, da, db = ref_wgrad(dyb, xb)
+    check_f32(a, ref, da, db, "wgrad split")
+    c = run_wgrad(dyb, xb, workspace=None)
+    check_f32(c, ref, da, db, "wgrad unsplit")
+
+
+def test_gemm_special_tiles():
+    """Zero tiles, negative-zero tiles, subnormal-scale tiles and exact E4M3
+    grids in both operands."""
+    M, N, K = 384, 256, 384
+    xb = inputs.random_bits((28,), (M, K), "special")
+    xb[5, :] = 0
+    xb[6, 128:256] = 0x8000
+    wb = inputs.random_bits((29,), (N, K), "special")
+    wb[:128, :128] = 0
+    y = run_fprop(xb, wb, "f32")
+    ref, a, b = ref_fprop(xb, wb)
+    check_f32(y, ref, a, b, "fprop special")
+    assert np.all(y[5] == 0)
+
+
+def test_every_code_passes_exactly():
+    """Rows of A hold all 254 finite codes; B rows are one-hot 1.0 (0x38) with
+    unit scales, so C[i][j] = dec(A[i][k_j]) * sA[i] exactly."""
+    t = oracle.e4m3_table()
+    finite = np.array([c for c in range(256) if not np.isnan(t[c])], dtype=np.uint8)
+    I, J, K = 256, 256, 256
+    rng = np.random.default_rng(40)
+    A = np.resize(finite, I * K).reshape(I, K).copy()
+    rng.shuffle(A, axis=1)
+    sA = np.ones((I, K // 128), np.float32)
+    kj = np.concatenate([np.arange(256)])
+    B = np.zeros((J, K), dtype=np.uint8)
+    B[np.arange(J), kj] = 0x38
+    sB = np.ones((J // 128, K // 128), np.float32)
+    dev = lambda a: torch.from_numpy(a).cuda()
+    y = fp8.fp8_gemm_fprop(dev(A), dev(sA), dev(B), dev(sB), out_dtype="f32")
+    torch.cuda.synchronize()
+    want = t[A[:, kj]].astype(np.float32)
+    got = to_np(y)
+    assert np.array_equal(got, want), np.argwhere(got != want)[:5]
+
+
+def test_gemm_empty_and_zero_contraction():
+    z = torch.empty((0, 256), dtype=torch.uint8, device="cuda")
+    zs = torch.empty((0, 2), dtype=torch.float32, device="cuda")
+    wq = torch.zeros((128, 256), dtype=torch.uint8, device="cuda")
+    ws = torch.ones((1, 2), dtype=torch.float32, device="cuda")
+    y = fp8.fp8_gemm_fprop(z, zs, wq, ws, out_dtype="f32")
+    assert y.shape == (0, 128)
+    # K == 0: the sum over no blocks is zero
+    xq = torch.empty((64, 0), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((64, 0), dtype=torch.float32, device="cuda")
+    wq0 = torch.empty((128, 0), dtype=torch.uint8, device="cuda")
+    ws0 = torch.empty((1, 0), dtype=torch.float32, device="cuda")
+    y = torch.full((64, 128), 7.0, device="cuda")
+    fp8.fp8_gemm_fprop(xq, xs, wq0, ws0, out_dtype="f32", y=y)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y).item() == 0
+
+
+def test_gemm_rerun_is_bitwise_identical():
+    M, N, K = 640, 512, 1024
+    xb = inputs.random_bits((30,), (M, K), "wide")
+    wb = inputs.normal((31,), (N, K), 0.02)
+    a = run_fprop(xb, wb, "f32")
+    b = run_fprop(xb, wb, "f32")
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))

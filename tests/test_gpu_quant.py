@@ -1,0 +1,184 @@
+"""GPU parity of the quantizers and the E4M3 conversion, through the C ABI,
+against the CPU oracle: codes and scales must be bit-identical."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp8_block_scaled_03_amd as fp8
+from fp8_block_scaled_03_amd import inputs
+from helpers import loaded_native_libs, to_dev_bf16, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def test_native_library_is_loaded():
+    fp8.capi()
+    libs = loaded_native_libs()
+    assert any(p.endswith("fp8_block_scaled_03_amd/libfp8bs.so") for p in libs), libs
+    assert torch.cuda.is_available()
+    assert "gfx950" in torch.cuda.get_device_properties(0).gcnArchName
+
+
+def _encode_gpu(v: np.ndarray) -> np.ndarray:
+    x = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).cuda()
+    q = fp8.fp8_encode_e4m3(x)
+    torch.cuda.synchronize()
+    return q.cpu().numpy()
+
+
+def test_conversion_ties_neighbours_and_specials():
+    t = oracle.e4m3_table()
+    mags = np.sort(t[:127])
+    mids = 0.5 * (mags[:-1] + mags[1:])
+    pts = np.concatenate([mags, mids, [448.0, 449.0, 464.0, 465.0, 1e6, 0.0]]).astype(np.float32)
+    v = np.concatenate([pts, np.nextafter(pts, np.float32(np.inf)),
+                        np.nextafter(pts, np.float32(-np.inf))]).astype(np.float32)
+    # FP32 subnormals and tiny normals
+    v = np.concatenate([v, np.array([1e-45, 1e-40, 1.1754942e-38, 1.1754944e-38, 2.0 ** -10,
+                                     2.0 ** -11], dtype=np.float32)])
+    v = np.concatenate([v, -v])
+    got = _encode_gpu(v)
+    want = oracle.e4m3_encode(np.clip(v, -448, 448))
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, [(float(v[i]), hex(got[i]), hex(want[i])) for i in bad[:10]]
+
+
+def test_conversion_strided_sweep():
+    # every 7th FP32 pattern with |v| <= 448*(1+2^-22), both signs (~330M values)
+    hi = int(np.float32(448.0).view(np.uint32)) + 2
+    step = 1 << 26
+    for lo in range(0, hi, step):
+        pats = np.arange(lo, min(lo + step, hi), 7, dtype=np.uint32)
+        v = pats.view(np.float32)
+        for sgn in (1.0, -1.0):
+            vv = (v * np.float32(sgn)).astype(np.float32)
+            got = _encode_gpu(vv)
+            want = oracle.e4m3_encode(vv)
+            if not np.array_equal(got, want):
+                i = np.flatnonzero(got != want)[:8]
+                pytest.fail(f"conversion mismatch at {[(float(vv[k]), hex(got[k]), hex(want[k])) for k in i]}")
+
+
+ROW_CASES = [
+    ("normal", 200, 384),        # ragged rows
+    ("wide", 1000, 512),
+    ("special", 129, 256),
+    ("normal", 1, 128),
+    ("wide", 4096, 2048),
+]
+
+
+def _rowtile_both(bits):
+    x = to_dev_bf16(bits)
+    q, s = fp8.fp8_quantize_rowtile(x)
+    torch.cuda.synchronize()
+    oq, os_ = oracle.quantize_rowtile(bits)
+    return to_np(q), to_np(s), oq, os_
+
+
+def _assert_codes(got_q, got_s, want_q, want_s, what):
+    if not np.array_equal(got_s.view(np.uint32), want_s.view(np.uint32)):
+        i = np.argwhere(got_s.view(np.uint32) != want_s.view(np.uint32))[:5]
+        pytest.fail(f"{what}: scales differ at {i.tolist()}: {got_s[tuple(i.T)]} vs {want_s[tuple(i.T)]}")
+    if not np.array_equal(got_q, want_q):
+        i = np.argwhere(got_q != want_q)[:5]
+        pytest.fail(f"{what}: codes differ at {i.tolist()}: "
+                    f"{[hex(c) for c in got_q[tuple(i.T)]]} vs {[hex(c) for c in want_q[tuple(i.T)]]}")
+
+
+@pytest.mark.parametrize("kind,M,K", ROW_CASES)
+def test_rowtile_parity(kind, M, K):
+    _say(f"rowtile {kind} {M}x{K}")
+    bits = inputs.random_bits((7, M, K), (M, K), kind)
+    _assert_codes(*_rowtile_both(bits), what=f"rowtile {kind} {M}x{K}")
+
+
+def test_rowtile_zero_and_negative_zero_tiles():
+    bits = np.zeros((3, 256), dtype=np.uint16)
+    bits[1, :128] = 0x8000
+    bits[2, 128:] = inputs.random_bits((8,), (1, 128), "special")[0]
+    _assert_codes(*_rowtile_both(bits), what="zero tiles")
+
+
+@pytest.mark.parametrize("cfg,name", [("qkv", "X"), ("mlp", "H"), ("down_bwd", "dY")])
+def test_rowtile_parity_config_tensors(cfg, name):
+    _say(f"rowtile config {cfg}.{name}")
+    bits = inputs.tensor(cfg, name)
+    _assert_codes(*_rowtile_both(bits), what=f"{cfg}.{name}")
+
+
+BLOCK_CASES = [("normal", 256, 512), ("wide", 384, 128), ("special", 128, 384)]
+
+
+def _block_both(bits, with_t=True):
+    w = to_dev_bf16(bits)
+    q, qt, s = fp8.fp8_quantize_block(w, with_transpose=with_t)
+    torch.cuda.synchronize()
+    oq, oqt, os_ = oracle.quantize_block(bits, with_transpose=with_t)
+    return q, qt, s, oq, oqt, os_
+
+
+@pytest.mark.parametrize("kind,N,K", BLOCK_CASES)
+def test_block_parity(kind, N, K):
+    bits = inputs.random_bits((9, N, K), (N, K), kind)
+    q, qt, s, oq, oqt, os_ = _block_both(bits)
+    _assert_codes(to_np(q), to_np(s), oq, os_, f"block {kind}")
+    assert np.array_equal(to_np(qt), oqt), "transposed weight codes differ"
+    # without the transposed copy the codes are the same
+    q2, qt2, s2, *_ = _block_both(bits, with_t=False)
+    assert qt2 is None and np.array_equal(to_np(q2), oq)
+
+
+@pytest.mark.parametrize("cfg,name", [("qkv", "W"), ("mlp", "W_gu"), ("down_bwd", "W_d")])
+def test_block_parity_config_weights(cfg, name):
+    bits = inputs.tensor(cfg, name)
+    q, qt, s, oq, oqt, os_ = _block_both(bits)
+    _assert_codes(to_np(q), to_np(s), oq, os_, f"{cfg}.{name}")
+    assert np.array_equal(to_np(qt), oqt)
+
+
+TR_CASES = [("normal", 128, 128), ("wide", 384, 256), ("special", 256, 640)]
+
+
+def _transposed_both(bits):
+    x = to_dev_bf16(bits)
+    qt, st = fp8.fp8_quantize_transposed(x)
+    torch.cuda.synchronize()
+    oqt, ost = oracle.quantize_transposed(bits)
+    return to_np(qt), to_np(st), oqt, ost
+
+
+@pytest.mark.parametrize("kind,M,C", TR_CASES)
+def test_transposed_parity(kind, M, C):
+    bits = inputs.random_bits((10, M, C), (M, C), kind)
+    _assert_codes(*_transposed_both(bits), what=f"transposed {kind} {M}x{C}")
+
+
+@pytest.mark.parametrize("cfg,name", [("down_bwd", "dY"), ("down_bwd", "H")])
+def test_transposed_parity_config_tensors(cfg, name):
+    _say(f"transposed config {cfg}.{name}")
+    bits = inputs.tensor(cfg, name)
+    _assert_codes(*_transposed_both(bits), what=f"{cfg}.{name}")
+
+
+def test_quantizers_are_deterministic():
+    bits = inputs.random_bits((11,), (512, 1024), "wide")
+    x = to_dev_bf16(bits)
+    a = fp8.fp8_quantize_rowtile(x)
+    b = fp8.fp8_quantize_rowtile(x)
+    c = fp8.fp8_quantize_transposed(x)
+    d = fp8.fp8_quantize_transposed(x)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert torch.equal(c[0], d[0]) and torch.equal(c[1], d[1])
+
+
+def test_empty_quantizer_calls():
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    q, s = fp8.fp8_quantize_rowtile(x)
+    assert q.shape == (0, 256) and s.shape == (0, 2)
