@@ -13,18 +13,19 @@
 // toward zero); on N(0,1)-like tiles that is a relative error of ~1.5e-5 per
 // block sum, far from FP32.  Every E4M3 value is exact in FP16, and the FP16
 // MFMA accumulates its products at FP32 precision, so the codes are widened
-// to FP16 in registers (v_cvt_scalef32_pk_f16_fp8, scale 1) and contracted
-// with v_mfma_f32_16x16x32_f16: four chained instructions give P for one
-// 128-wide block in FP32, which is folded into the FP32 accumulator with one
-// FMA per output element (acc += P * sA*sB).
+// to FP16 (v_cvt_scalef32_pk_f16_fp8, scale 1) and contracted with
+// v_mfma_f32_16x16x32_f16: four chained instructions give P for one 128-wide
+// block in FP32, which is folded into the FP32 accumulator with one FMA per
+// output element (acc += P * sA*sB).
 //
 // Workgroup tile 128 (i) x 128 (j) x 128 (k), four waves in a 2x2 grid, each
-// wave a 64x64 patch of 4x4 MFMA tiles.  FP8 tiles are staged in LDS (double
-// buffered, 16-byte chunks XOR-swizzled by row so the fragment reads are
-// bank-conflict free); the next block's global loads are issued before the
-// current block's MFMAs.  The MFMA operands are swapped (B tile as the first
-// source) so that each lane owns four consecutive output columns of one row
-// and stores them as one vector.
+// wave a 64x64 patch of 4x4 MFMA tiles; two workgroups share a CU.  Each
+// thread loads its share of the next block's FP8 codes into registers while
+// the current block is contracted; the codes are widened to FP16 once, as
+// they are stored to LDS (16-byte chunks XOR-swizzled by row so the fragment
+// reads are bank-conflict free).  The MFMA operands are swapped (B tile as
+// the first source) so that each lane owns four consecutive output columns of
+// one row and stores them as one vector.
 #include "device_common.h"
 #include "internal.h"
 
@@ -47,20 +48,30 @@ constexpr int kBM = 128;
 constexpr int kBN = 128;
 constexpr int kBK = 128;
 constexpr int kThreads = 256;
+constexpr int kTileBytes = kBM * kBK;       // one FP8 operand tile: 16 KB
 
-__device__ __forceinline__ int swz(int row, int chunk) {
-    return row * kBK + ((chunk ^ (row & 7)) << 4);
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Byte offset of 16-byte chunk c (0..7, K = 16c .. 16c+15) of tile row r.  The
+// chunk index is XORed with bits 1..3 of the row, so that the 16 lanes served
+// together by a 16-byte LDS read (16 consecutive rows, one logical chunk)
+// cover all 64 banks exactly once.
+__device__ __forceinline__ int lds_off(int row, int c) {
+    return row * kBK + ((c ^ ((row >> 1) & 7)) << 4);
 }
 
+// vmcnt(0): this wave's global loads (including those into LDS) have landed.
+__device__ __forceinline__ void wait_global_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <int MODE, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads) void gemm_bs_fp8_kernel(
+__global__ __launch_bounds__(kThreads, 2) void gemm_bs_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
     const float* __restrict__ sB, void* __restrict__ C, int64_t I, int64_t J, int64_t Kc,
     int tiles_j) {
-    __shared__ __align__(16) uint8_t As[2][kBM * kBK];
-    __shared__ __align__(16) uint8_t Bs[2][kBN * kBK];
-    __shared__ float sAs[2][kBM];
-    __shared__ float sBs[2][kBN];
+    __shared__ __align__(16) uint8_t As[2][kTileBytes];
+    __shared__ __align__(16) uint8_t Bs[2][kTileBytes];
+    __shared__ __align__(16) float sAs[2][kBM];
+    __shared__ __align__(16) float sBs[2][kBN];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -71,50 +82,45 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_fp8_kernel(
     const int nkb = (int)(Kc / kBK);
     const int64_t jb_count = J / kBN;
 
-    // global -> register staging (4 chunks of A and 4 of B per thread)
-    uint4 ra[4], rb[4];
-    float rsa = 0.f, rsb = 0.f;
-    const uint8_t* a_rows[4];
-    const uint8_t* b_rows[4];
+    // Direct global -> LDS loads: wave w fills 1 KB pieces 4w .. 4w+3 of each
+    // tile (8 rows each).  Lane l lands at LDS slot l of its piece, i.e. row
+    // 8*piece + l/8, physical chunk l%8, so it fetches the logical chunk that
+    // the swizzle puts there.
+    const uint8_t* a_src[4];
+    const uint8_t* b_src[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        int id = q * kThreads + tid;
-        int row = id >> 3, c = id & 7;
-        int64_t gi = min(i0 + row, I - 1);
-        a_rows[q] = A + gi * Kc + c * 16;
-        b_rows[q] = B + (j0 + row) * Kc + c * 16;
+    for (int j = 0; j < 4; ++j) {
+        int row = 8 * (4 * wave + j) + (lane >> 3);
+        int c = (lane & 7) ^ ((row >> 1) & 7);
+        a_src[j] = A + min(i0 + row, I - 1) * Kc + c * 16;
+        b_src[j] = B + (j0 + row) * Kc + c * 16;
     }
-    const float* sa_ptr = sA + min(i0 + (tid & 127), I - 1) * nkb;
+    // Scales: waves 0/1 load the A-row scales of rows 64w + lane, waves 2/3 the
+    // B scales (per row for wgrad, one block scale otherwise).
+    const float* s_src;
+    if (wave < 2) {
+        s_src = sA + min(i0 + 64 * wave + lane, I - 1) * nkb;
+    } else if (MODE == kScaleRow) {
+        s_src = sB + (j0 + 64 * (wave - 2) + lane) * nkb;
+    } else if (MODE == kScaleBlock) {
+        s_src = sB + (int64_t)tj * nkb;
+    } else {
+        s_src = sB + tj;            // + kb * jb_count below
+    }
 
-    auto load_global = [&](int kb) {
+    auto issue_loads = [&](int kb, int buf) {
+        const int64_t koff = (int64_t)kb * kBK;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            ra[q] = *reinterpret_cast<const uint4*>(a_rows[q] + (int64_t)kb * kBK);
-            rb[q] = *reinterpret_cast<const uint4*>(b_rows[q] + (int64_t)kb * kBK);
+        for (int j = 0; j < 4; ++j) {
+            __builtin_amdgcn_global_load_lds(a_src[j] + koff,
+                                             (lds_void*)(&As[buf][(4 * wave + j) * 1024]), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(b_src[j] + koff,
+                                             (lds_void*)(&Bs[buf][(4 * wave + j) * 1024]), 16, 0, 0);
         }
-        if (tid < 128) {
-            rsa = sa_ptr[kb];
-        } else {
-            if (MODE == kScaleRow)
-                rsb = sB[(j0 + (tid - 128)) * nkb + kb];
-            else if (MODE == kScaleBlock)
-                rsb = sB[(int64_t)tj * nkb + kb];
-            else
-                rsb = sB[(int64_t)kb * jb_count + tj];
-        }
-    };
-    auto store_lds = [&](int buf) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            int id = q * kThreads + tid;
-            int row = id >> 3, c = id & 7;
-            *reinterpret_cast<uint4*>(&As[buf][swz(row, c)]) = ra[q];
-            *reinterpret_cast<uint4*>(&Bs[buf][swz(row, c)]) = rb[q];
-        }
-        if (tid < 128)
-            sAs[buf][tid] = rsa;
-        else
-            sBs[buf][tid - 128] = rsb;
+        const float* sp = (MODE == kScaleBlockT && wave >= 2) ? s_src + (int64_t)kb * jb_count
+                                                               : s_src + kb;
+        float* sdst = (wave < 2) ? &sAs[buf][64 * wave] : &sBs[buf][64 * (wave - 2)];
+        __builtin_amdgcn_global_load_lds(sp, (lds_void*)sdst, 4, 0, 0);
     };
 
     v4f acc[4][4];
@@ -126,80 +132,79 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_fp8_kernel(
     const int r16 = lane & 15;
     const int g = lane >> 4;
 
-    if (nkb > 0) {
-        load_global(0);
-        store_lds(0);
-        __syncthreads();
-    }
+    if (nkb > 0) issue_loads(0, 0);
     for (int kb = 0; kb < nkb; ++kb) {
         const int buf = kb & 1;
-        if (kb + 1 < nkb) load_global(kb + 1);
+        wait_global_loads();
+        __syncthreads();          // block kb is in LDS; everyone is done with buf^1
+        if (kb + 1 < nkb) issue_loads(kb + 1, buf ^ 1);
 
-        // raw codes: lane (r16, g) holds bytes [32g, 32g+32) of row r16 of a 16-row subtile
-        uint4 a_lo[4], a_hi[4], b_lo[4], b_hi[4];
+        const uint8_t* At = As[buf];
+        const uint8_t* Bt = Bs[buf];
+        v4f p[4][4];
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            int row = wi * 64 + it * 16 + r16;
-            a_lo[it] = *reinterpret_cast<const uint4*>(&As[buf][swz(row, 2 * g)]);
-            a_hi[it] = *reinterpret_cast<const uint4*>(&As[buf][swz(row, 2 * g + 1)]);
-        }
+        for (int it = 0; it < 4; ++it)
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-            int row = wj * 64 + jt * 16 + r16;
-            b_lo[jt] = *reinterpret_cast<const uint4*>(&Bs[buf][swz(row, 2 * g)]);
-            b_hi[jt] = *reinterpret_cast<const uint4*>(&Bs[buf][swz(row, 2 * g + 1)]);
-        }
-        // FP16 fragments: chunk c (0..3) of a lane is bytes [8c, 8c+8) of its 32 bytes;
-        // A and B use the same byte -> K assignment, so each 4-MFMA chain sums the
-        // whole 128-wide block.
-        v8h af[4][4], bfr[4][4];
+            for (int jt = 0; jt < 4; ++jt) p[it][jt] = v4f{0.f, 0.f, 0.f, 0.f};
+        // Lane (r16, g) holds bytes [32g, 32g+32) of its row of each 16-row
+        // subtile, read as two 16-byte halves h.  MFMA chunk c = 2h + e takes
+        // bytes [8c, 8c+8) of them for A and B alike, so the 4-instruction chain
+        // covers every K of the block once.
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            af[it][0] = widen8(a_lo[it].x, a_lo[it].y);
-            af[it][1] = widen8(a_lo[it].z, a_lo[it].w);
-            af[it][2] = widen8(a_hi[it].x, a_hi[it].y);
-            af[it][3] = widen8(a_hi[it].z, a_hi[it].w);
-        }
+        for (int h = 0; h < 2; ++h) {
+            uint4 ar[4], br[4];
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-            bfr[jt][0] = widen8(b_lo[jt].x, b_lo[jt].y);
-            bfr[jt][1] = widen8(b_lo[jt].z, b_lo[jt].w);
-            bfr[jt][2] = widen8(b_hi[jt].x, b_hi[jt].y);
-            bfr[jt][3] = widen8(b_hi[jt].z, b_hi[jt].w);
+            for (int it = 0; it < 4; ++it)
+                ar[it] = *reinterpret_cast<const uint4*>(At + lds_off(wi * 64 + it * 16 + r16, 2 * g + h));
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt)
+                br[jt] = *reinterpret_cast<const uint4*>(Bt + lds_off(wj * 64 + jt * 16 + r16, 2 * g + h));
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                v8h af[4], bf[4];
+#pragma unroll
+                for (int it = 0; it < 4; ++it)
+                    af[it] = e ? widen8(ar[it].z, ar[it].w) : widen8(ar[it].x, ar[it].y);
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt)
+                    bf[jt] = e ? widen8(br[jt].z, br[jt].w) : widen8(br[jt].x, br[jt].y);
+#pragma unroll
+                for (int it = 0; it < 4; ++it)
+#pragma unroll
+                    for (int jt = 0; jt < 4; ++jt)
+                        // D[j][i]: j = 4g+v (rows of the B subtile), i = r16 (rows of the A subtile)
+                        p[it][jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[jt], af[it], p[it][jt],
+                                                                            0, 0, 0);
+            }
         }
+        // fold: acc += P * sA(i) * sB(j)
         float sa[4];
 #pragma unroll
         for (int it = 0; it < 4; ++it) sa[it] = sAs[buf][wi * 64 + it * 16 + r16];
         if (MODE != kScaleRow) {
             const float sb = sBs[buf][0];
 #pragma unroll
-            for (int it = 0; it < 4; ++it) sa[it] = sa[it] * sb;
-        }
-        float sbv[4][4];
-        if (MODE == kScaleRow) {
+            for (int it = 0; it < 4; ++it) {
+                const float cs = sa[it] * sb;
 #pragma unroll
-            for (int jt = 0; jt < 4; ++jt)
+                for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) sbv[jt][v] = sBs[buf][wj * 64 + jt * 16 + 4 * g + v];
-        }
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
+                    for (int v = 0; v < 4; ++v)
+                        acc[it][jt][v] = __builtin_fmaf(p[it][jt][v], cs, acc[it][jt][v]);
+            }
+        } else {
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt) {
-                // D[j][i] with j = 4g+v (rows of the B subtile), i = r16 (rows of the A subtile)
-                v4f p = v4f{0.f, 0.f, 0.f, 0.f};
+                const float4 sb = *reinterpret_cast<const float4*>(&sBs[buf][wj * 64 + jt * 16 + 4 * g]);
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    p = __builtin_amdgcn_mfma_f32_16x16x32_f16(bfr[jt][c], af[it][c], p, 0, 0, 0);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    float c = (MODE == kScaleRow) ? sa[it] * sbv[jt][v] : sa[it];
-                    acc[it][jt][v] = __builtin_fmaf(p[v], c, acc[it][jt][v]);
+                for (int it = 0; it < 4; ++it) {
+                    acc[it][jt][0] = __builtin_fmaf(p[it][jt][0], sa[it] * sb.x, acc[it][jt][0]);
+                    acc[it][jt][1] = __builtin_fmaf(p[it][jt][1], sa[it] * sb.y, acc[it][jt][1]);
+                    acc[it][jt][2] = __builtin_fmaf(p[it][jt][2], sa[it] * sb.z, acc[it][jt][2]);
+                    acc[it][jt][3] = __builtin_fmaf(p[it][jt][3], sa[it] * sb.w, acc[it][jt][3]);
                 }
             }
         }
-        if (kb + 1 < nkb) store_lds(buf ^ 1);
-        __syncthreads();
     }
 
     // epilogue: lane owns C[i][j .. j+3]
