@@ -26,6 +26,9 @@
 // reads are bank-conflict free).  The MFMA operands are swapped (B tile as
 // the first source) so that each lane owns four consecutive output columns of
 // one row and stores them as one vector.
+#include <cstdlib>
+#include <cstring>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -67,7 +70,7 @@ template <int MODE, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads, 2) void gemm_bs_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
     const float* __restrict__ sB, void* __restrict__ C, int64_t I, int64_t J, int64_t Kc,
-    int tiles_j) {
+    int tiles_j, int nps) {
     __shared__ __align__(16) uint8_t As[2][kTileBytes];
     __shared__ __align__(16) uint8_t Bs[2][kTileBytes];
     __shared__ __align__(16) float sAs[2][kBM];
@@ -79,7 +82,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bs_fp8_kernel(
     const int wi = wave & 1, wj = wave >> 1;
     const int ti = blockIdx.x / tiles_j, tj = blockIdx.x % tiles_j;
     const int64_t i0 = (int64_t)ti * kBM, j0 = (int64_t)tj * kBN;
-    const int nkb = (int)(Kc / kBK);
+    const int nkb_all = (int)(Kc / kBK);
+    const int kb0 = blockIdx.y * nps;                 // split s: blocks [s*nps, (s+1)*nps)
+    const int nkb = min(nkb_all, kb0 + nps) - kb0;
     const int64_t jb_count = J / kBN;
 
     // Direct global -> LDS loads: wave w fills 1 KB pieces 4w .. 4w+3 of each
@@ -99,11 +104,11 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bs_fp8_kernel(
     // B scales (per row for wgrad, one block scale otherwise).
     const float* s_src;
     if (wave < 2) {
-        s_src = sA + min(i0 + 64 * wave + lane, I - 1) * nkb;
+        s_src = sA + min(i0 + 64 * wave + lane, I - 1) * nkb_all;
     } else if (MODE == kScaleRow) {
-        s_src = sB + (j0 + 64 * (wave - 2) + lane) * nkb;
+        s_src = sB + (j0 + 64 * (wave - 2) + lane) * nkb_all;
     } else if (MODE == kScaleBlock) {
-        s_src = sB + (int64_t)tj * nkb;
+        s_src = sB + (int64_t)tj * nkb_all;
     } else {
         s_src = sB + tj;            // + kb * jb_count below
     }
@@ -132,12 +137,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bs_fp8_kernel(
     const int r16 = lane & 15;
     const int g = lane >> 4;
 
-    if (nkb > 0) issue_loads(0, 0);
-    for (int kb = 0; kb < nkb; ++kb) {
-        const int buf = kb & 1;
+    if (nkb > 0) issue_loads(kb0, 0);
+    for (int k = 0; k < nkb; ++k) {
+        const int buf = k & 1;
         wait_global_loads();
-        __syncthreads();          // block kb is in LDS; everyone is done with buf^1
-        if (kb + 1 < nkb) issue_loads(kb + 1, buf ^ 1);
+        __syncthreads();          // this block is in LDS; everyone is done with buf^1
+        if (k + 1 < nkb) issue_loads(kb0 + k + 1, buf ^ 1);
 
         const uint8_t* At = As[buf];
         const uint8_t* Bt = Bs[buf];
@@ -222,7 +227,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bs_fp8_kernel(
                 pk.y = f32_to_bf16_rne(acc[it][jt][2]) | (f32_to_bf16_rne(acc[it][jt][3]) << 16);
                 *reinterpret_cast<uint2*>(Cb + i * J + j) = pk;
             } else {
-                float* Cf = reinterpret_cast<float*>(C);
+                float* Cf = reinterpret_cast<float*>(C) + (int64_t)blockIdx.y * I * J;
                 *reinterpret_cast<float4*>(Cf + i * J + j) =
                     make_float4(acc[it][jt][0], acc[it][jt][1], acc[it][jt][2], acc[it][jt][3]);
             }
@@ -230,33 +235,344 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bs_fp8_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile kernel: workgroup tile 256 (i) x 256 (j) x 128 (k), eight waves
+// in a 4 (i) x 2 (j) grid, each wave a 64 x 128 patch.  A wave widens its 64
+// A rows to FP16 once per block and keeps them in registers (64 VGPRs), then
+// streams its eight 16-row B subtiles: per subtile it widens one 8-code chunk
+// at a time and runs the 4-instruction MFMA chain for its four A subtiles, so
+// 192 widenings feed 128 MFMAs (1.5 per MFMA, against 2 in the small kernel).
+// Tiles are ordered for the L2s: each XCD (the hardware deals workgroups to
+// the eight XCDs round-robin) gets a contiguous chunk of the tile order, and
+// the order walks groups of four tile rows column by column, so the tiles an
+// XCD runs together share A and B rows.  gridDim.y splits the contraction:
+// split s sums blocks [s*nps, (s+1)*nps) into its own FP32 slice of C.
+// ---------------------------------------------------------------------------
+constexpr int kBigM = 256;
+constexpr int kBigN = 256;
+constexpr int kBigThreads = 512;
+constexpr int kBigTile = kBigM * kBK;      // one FP8 operand tile: 32 KB
+constexpr int kGroupRows = 4;
+
+__device__ __forceinline__ void tile_coords(int bid, int tiles_i, int tiles_j, int* ti, int* tj) {
+    const int T = tiles_i * tiles_j;
+    int t = bid;
+    if ((T & 7) == 0) t = (bid & 7) * (T >> 3) + (bid >> 3);      // contiguous chunk per XCD
+    const int per_group = kGroupRows * tiles_j;
+    const int grp = t / per_group;
+    const int rows = min(kGroupRows, tiles_i - grp * kGroupRows);
+    const int r = t - grp * per_group;
+    *ti = grp * kGroupRows + r % rows;
+    *tj = r / rows;
+}
+
+template <int MODE, bool OUT_BF16>
+__global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
+    const float* __restrict__ sB, void* __restrict__ C, int64_t I, int64_t J, int64_t Kc,
+    int tiles_i, int tiles_j, int nps) {
+    __shared__ __align__(16) uint8_t As[2][kBigTile];
+    __shared__ __align__(16) uint8_t Bs[2][kBigTile];
+    __shared__ __align__(16) float sAs[2][kBigM];
+    __shared__ __align__(16) float sBs[2][kBigN];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wi = wave & 3, wj = wave >> 2;
+    int ti, tj;
+    tile_coords(blockIdx.x, tiles_i, tiles_j, &ti, &tj);
+    const int64_t i0 = (int64_t)ti * kBigM, j0 = (int64_t)tj * kBigN;
+    const int nkb_all = (int)(Kc / kBK);
+    const int kb0 = blockIdx.y * nps;
+    const int kb1 = min(nkb_all, kb0 + nps);
+    const int nkb = kb1 - kb0;
+    const int nkb_row = nkb_all;                  // scale row stride (blocks per row)
+    const int64_t jb_count = J / kBN;             // 128-wide column blocks of B
+
+    // Direct global -> LDS loads: wave w fills 1 KB pieces 4w .. 4w+3 of each
+    // 32 KB tile (8 rows each), lane l landing at row 8*piece + l/8, physical
+    // chunk l%8 of the swizzle.
+    const uint8_t* a_src[4];
+    const uint8_t* b_src[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        int row = 8 * (4 * wave + j) + (lane >> 3);
+        int c = (lane & 7) ^ ((row >> 1) & 7);
+        a_src[j] = A + min(i0 + row, I - 1) * Kc + c * 16;
+        b_src[j] = B + min(j0 + row, J - 1) * Kc + c * 16;
+    }
+    // Scales: waves 0..3 load the A-row scales of rows 64w + lane, waves 4..7
+    // the B scales of rows 64(w-4) + lane (per row, or their column block's).
+    const float* s_src;
+    int64_t s_step;                               // stride per contraction block
+    if (wave < 4) {
+        s_src = sA + min(i0 + 64 * wave + lane, I - 1) * nkb_row;
+        s_step = 1;
+    } else {
+        int64_t jr = min(j0 + 64 * (wave - 4) + lane, J - 1);
+        if (MODE == kScaleRow) {
+            s_src = sB + jr * nkb_row;
+            s_step = 1;
+        } else if (MODE == kScaleBlock) {
+            s_src = sB + (jr / kBN) * nkb_row;
+            s_step = 1;
+        } else {
+            s_src = sB + jr / kBN;
+            s_step = jb_count;
+        }
+    }
+
+    auto issue_loads = [&](int kb, int buf) {
+        const int64_t koff = (int64_t)kb * kBK;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            __builtin_amdgcn_global_load_lds(a_src[j] + koff,
+                                             (lds_void*)(&As[buf][(4 * wave + j) * 1024]), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(b_src[j] + koff,
+                                             (lds_void*)(&Bs[buf][(4 * wave + j) * 1024]), 16, 0, 0);
+        }
+        float* sdst = (wave < 4) ? &sAs[buf][64 * wave] : &sBs[buf][64 * (wave - 4)];
+        __builtin_amdgcn_global_load_lds(s_src + kb * s_step, (lds_void*)sdst, 4, 0, 0);
+    };
+
+    v4f acc[4][8];
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int js = 0; js < 8; ++js) acc[it][js] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const int r16 = lane & 15;
+    const int g = lane >> 4;
+
+    if (nkb > 0) issue_loads(kb0, 0);
+    for (int k = 0; k < nkb; ++k) {
+        const int buf = k & 1;
+        wait_global_loads();
+        __syncthreads();
+        if (k + 1 < nkb) issue_loads(kb0 + k + 1, buf ^ 1);
+
+        const uint8_t* At = As[buf];
+        const uint8_t* Bt = Bs[buf];
+        // This wave's A rows for the whole block, widened once: af[it][c] is
+        // MFMA chunk c (bytes [8c, 8c+8) of the lane's 32) of subtile it.
+        v8h af[4][4];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int row = wi * 64 + it * 16 + r16;
+            uint4 lo = *reinterpret_cast<const uint4*>(At + lds_off(row, 2 * g));
+            uint4 hi = *reinterpret_cast<const uint4*>(At + lds_off(row, 2 * g + 1));
+            af[it][0] = widen8(lo.x, lo.y);
+            af[it][1] = widen8(lo.z, lo.w);
+            af[it][2] = widen8(hi.x, hi.y);
+            af[it][3] = widen8(hi.z, hi.w);
+        }
+        float sa[4];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) sa[it] = sAs[buf][wi * 64 + it * 16 + r16];
+        if (MODE != kScaleRow) {
+            const float sb = sBs[buf][128 * wj];      // the wave's 128 columns share one block scale
+#pragma unroll
+            for (int it = 0; it < 4; ++it) sa[it] = sa[it] * sb;
+        }
+#pragma unroll
+        for (int js = 0; js < 8; ++js) {
+            const int row = wj * 128 + js * 16 + r16;
+            uint4 lo = *reinterpret_cast<const uint4*>(Bt + lds_off(row, 2 * g));
+            uint4 hi = *reinterpret_cast<const uint4*>(Bt + lds_off(row, 2 * g + 1));
+            v4f p[4];
+#pragma unroll
+            for (int it = 0; it < 4; ++it) p[it] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t w0 = c == 0 ? lo.x : c == 1 ? lo.z : c == 2 ? hi.x : hi.z;
+                const uint32_t w1 = c == 0 ? lo.y : c == 1 ? lo.w : c == 2 ? hi.y : hi.w;
+                const v8h bf = widen8(w0, w1);
+#pragma unroll
+                for (int it = 0; it < 4; ++it)
+                    p[it] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf, af[it][c], p[it], 0, 0, 0);
+            }
+            if (MODE != kScaleRow) {
+#pragma unroll
+                for (int it = 0; it < 4; ++it)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        acc[it][js][v] = __builtin_fmaf(p[it][v], sa[it], acc[it][js][v]);
+            } else {
+                const float4 sb =
+                    *reinterpret_cast<const float4*>(&sBs[buf][wj * 128 + js * 16 + 4 * g]);
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    acc[it][js][0] = __builtin_fmaf(p[it][0], sa[it] * sb.x, acc[it][js][0]);
+                    acc[it][js][1] = __builtin_fmaf(p[it][1], sa[it] * sb.y, acc[it][js][1]);
+                    acc[it][js][2] = __builtin_fmaf(p[it][2], sa[it] * sb.z, acc[it][js][2]);
+                    acc[it][js][3] = __builtin_fmaf(p[it][3], sa[it] * sb.w, acc[it][js][3]);
+                }
+            }
+        }
+    }
+
+    // epilogue: lane owns C[i][j .. j+3]; split s writes its own FP32 slice
+    if (j0 + 128 * wj >= J) return;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int64_t i = i0 + wi * 64 + it * 16 + r16;
+        if (i >= I) continue;
+#pragma unroll
+        for (int js = 0; js < 8; ++js) {
+            const int64_t j = j0 + wj * 128 + js * 16 + 4 * g;
+            if (OUT_BF16) {
+                uint16_t* Cb = reinterpret_cast<uint16_t*>(C);
+                uint2 pk;
+                pk.x = f32_to_bf16_rne(acc[it][js][0]) | (f32_to_bf16_rne(acc[it][js][1]) << 16);
+                pk.y = f32_to_bf16_rne(acc[it][js][2]) | (f32_to_bf16_rne(acc[it][js][3]) << 16);
+                *reinterpret_cast<uint2*>(Cb + i * J + j) = pk;
+            } else {
+                float* Cf = reinterpret_cast<float*>(C) + (int64_t)blockIdx.y * I * J;
+                *reinterpret_cast<float4*>(Cf + i * J + j) =
+                    make_float4(acc[it][js][0], acc[it][js][1], acc[it][js][2], acc[it][js][3]);
+            }
+        }
+    }
+}
+
+// Sum of the split slices, in split order: out[e] = sum_s ws[s][e] (fixed order,
+// so the result does not depend on timing).
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float4* __restrict__ ws,
+                                                            float4* __restrict__ out, int64_t n4,
+                                                            int splits) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= n4) return;
+    float4 a = ws[e];
+    for (int s = 1; s < splits; ++s) {
+        const float4 b = ws[(int64_t)s * n4 + e];
+        a.x += b.x;
+        a.y += b.y;
+        a.z += b.z;
+        a.w += b.w;
+    }
+    out[e] = a;
+}
+
 template <int MODE, bool BF16>
-static hipError_t launch_t(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB,
-                           void* C, int64_t I, int64_t J, int64_t Kc, hipStream_t stream) {
+static hipError_t launch_small(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB,
+                               void* C, int64_t I, int64_t J, int64_t Kc, int splits, int nps,
+                               hipStream_t stream) {
     int64_t tiles_i = (I + kBM - 1) / kBM;
     int64_t tiles_j = J / kBN;
     int64_t blocks = tiles_i * tiles_j;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((gemm_bs_fp8_kernel<MODE, BF16>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                       stream, A, sA, B, sB, C, I, J, Kc, (int)tiles_j);
+    hipLaunchKernelGGL((gemm_bs_fp8_kernel<MODE, BF16>), dim3((unsigned)blocks, splits),
+                       dim3(kThreads), 0, stream, A, sA, B, sB, C, I, J, Kc, (int)tiles_j, nps);
     return hipGetLastError();
 }
 
-size_t gemm_workspace_bytes(ScaleMode, int64_t, int64_t, int64_t, int) { return 0; }
+template <int MODE, bool BF16>
+static hipError_t launch_big(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB,
+                             void* C, int64_t I, int64_t J, int64_t Kc, int splits, int nps,
+                             hipStream_t stream) {
+    int tiles_i = (int)((I + kBigM - 1) / kBigM);
+    int tiles_j = (int)((J + kBigN - 1) / kBigN);
+    hipLaunchKernelGGL((gemm_bs_fp8_big_kernel<MODE, BF16>), dim3(tiles_i * tiles_j, splits),
+                       dim3(kBigThreads), 0, stream, A, sA, B, sB, C, I, J, Kc, tiles_i, tiles_j,
+                       nps);
+    return hipGetLastError();
+}
+
+// Launch plan for one GEMM: which kernel, and how many contraction splits.
+struct Plan {
+    bool big;
+    int splits;
+    int nps;     // contraction blocks per split
+};
+
+// FP8BS_GEMM_KERNEL=small|big forces one kernel (a testing aid; the default
+// "auto" picks the large tile when it yields at least one tile per CU).  Read
+// on every call so a test can switch it between calls.
+static int kernel_override() {
+    const char* e = getenv("FP8BS_GEMM_KERNEL");
+    if (!e) return 0;
+    if (!strcmp(e, "small")) return 1;
+    if (!strcmp(e, "big")) return 2;
+    return 0;
+}
+
+static Plan plan_gemm(ScaleMode mode, int64_t I, int64_t J, int64_t Kc, int num_cus,
+                      bool allow_split) {
+    Plan p{false, 1, (int)(Kc / kBK)};
+    const int64_t nkb = Kc / kBK;
+    const int cus = num_cus > 0 ? num_cus : 256;
+    const int force = kernel_override();
+    if (nkb == 0) return p;
+    const int64_t big_tiles = ((I + kBigM - 1) / kBigM) * ((J + kBigN - 1) / kBigN);
+    const int64_t small_tiles = ((I + kBM - 1) / kBM) * (J / kBN);
+    // fprop/dgrad: the 256x256 tile once it gives every CU a tile.  wgrad (two
+    // per-row scales, so two VALU operations per output in the fold): the
+    // 128x128 tile, whose lighter register use suits that fold better.
+    if (force == 2) p.big = true;
+    else if (force == 1) p.big = false;
+    else p.big = (mode != kScaleRow) && I >= kBigM && big_tiles >= cus;
+    // Split the contraction when the tiles cannot fill the CUs twice over
+    // (FP32 output only, with a caller workspace).
+    if (mode == kScaleRow && allow_split) {
+        const int64_t tiles = p.big ? big_tiles : small_tiles;
+        const int64_t target = p.big ? 2 * cus : 4 * cus;     // workgroups in flight: 1 or 2 per CU
+        int s = 1;
+        while (tiles * s < target && nkb / (2 * s) >= 4) s *= 2;
+        if (s > 1) {
+            p.nps = (int)((nkb + s - 1) / s);
+            p.splits = (int)((nkb + p.nps - 1) / p.nps);
+        }
+    }
+    return p;
+}
+
+size_t gemm_workspace_bytes(ScaleMode mode, int64_t I, int64_t J, int64_t Kc, int num_cus) {
+    Plan p = plan_gemm(mode, I, J, Kc, num_cus, true);
+    if (p.splits <= 1) return 0;
+    return (size_t)p.splits * (size_t)I * (size_t)J * sizeof(float);
+}
+
+template <int MODE>
+static hipError_t launch_mode(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB,
+                              void* C, bool out_bf16, int64_t I, int64_t J, int64_t Kc,
+                              void* workspace, size_t workspace_bytes, int num_cus,
+                              hipStream_t stream) {
+    const size_t need = gemm_workspace_bytes((ScaleMode)MODE, I, J, Kc, num_cus);
+    const bool can_split = !out_bf16 && workspace && need > 0 && workspace_bytes >= need;
+    Plan p = plan_gemm((ScaleMode)MODE, I, J, Kc, num_cus, can_split);
+    if (p.splits <= 1) {
+        if (p.big)
+            return out_bf16 ? launch_big<MODE, true>(A, sA, B, sB, C, I, J, Kc, 1, p.nps, stream)
+                            : launch_big<MODE, false>(A, sA, B, sB, C, I, J, Kc, 1, p.nps, stream);
+        return out_bf16 ? launch_small<MODE, true>(A, sA, B, sB, C, I, J, Kc, 1, p.nps, stream)
+                        : launch_small<MODE, false>(A, sA, B, sB, C, I, J, Kc, 1, p.nps, stream);
+    }
+    hipError_t e = p.big ? launch_big<MODE, false>(A, sA, B, sB, workspace, I, J, Kc, p.splits,
+                                                   p.nps, stream)
+                         : launch_small<MODE, false>(A, sA, B, sB, workspace, I, J, Kc, p.splits,
+                                                     p.nps, stream);
+    if (e != hipSuccess) return e;
+    const int64_t n4 = I * J / 4;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0,
+                       stream, reinterpret_cast<const float4*>(workspace),
+                       reinterpret_cast<float4*>(C), n4, p.splits);
+    return hipGetLastError();
+}
 
 hipError_t launch_gemm(ScaleMode mode, const uint8_t* A, const float* sA, const uint8_t* B,
                        const float* sB, void* C, bool out_bf16, int64_t I, int64_t J, int64_t Kc,
-                       void*, size_t, int, hipStream_t stream) {
+                       void* workspace, size_t workspace_bytes, int num_cus, hipStream_t stream) {
     switch (mode) {
         case kScaleBlock:
-            return out_bf16 ? launch_t<kScaleBlock, true>(A, sA, B, sB, C, I, J, Kc, stream)
-                            : launch_t<kScaleBlock, false>(A, sA, B, sB, C, I, J, Kc, stream);
+            return launch_mode<kScaleBlock>(A, sA, B, sB, C, out_bf16, I, J, Kc, workspace,
+                                            workspace_bytes, num_cus, stream);
         case kScaleBlockT:
-            return out_bf16 ? launch_t<kScaleBlockT, true>(A, sA, B, sB, C, I, J, Kc, stream)
-                            : launch_t<kScaleBlockT, false>(A, sA, B, sB, C, I, J, Kc, stream);
+            return launch_mode<kScaleBlockT>(A, sA, B, sB, C, out_bf16, I, J, Kc, workspace,
+                                             workspace_bytes, num_cus, stream);
         case kScaleRow:
-            return out_bf16 ? launch_t<kScaleRow, true>(A, sA, B, sB, C, I, J, Kc, stream)
-                            : launch_t<kScaleRow, false>(A, sA, B, sB, C, I, J, Kc, stream);
+            return launch_mode<kScaleRow>(A, sA, B, sB, C, out_bf16, I, J, Kc, workspace,
+                                          workspace_bytes, num_cus, stream);
     }
     return hipErrorInvalidValue;
 }

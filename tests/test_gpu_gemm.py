@@ -14,6 +14,13 @@ from helpers import check_bf16, check_f32, to_dev_bf16, to_np
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(params=["small", "big"])
+def kernel(request, monkeypatch):
+    """Run the test with the 128x128 and with the 256x256 GEMM kernel."""
+    monkeypatch.setenv("FP8BS_GEMM_KERNEL", request.param)
+    return request.param
+
+
 def _say(*a):
     print(*a, flush=True)
 
@@ -67,18 +74,19 @@ def ref_wgrad(dybits, xbits, rows=None):
     return dw, oracle.dequantize_rows(dytq, dyts), oracle.dequantize_rows(xtq, xts)
 
 
-FPROP_CASES = [  # (M, N, K) -- ragged M, several tiles in every direction
-    (256, 256, 512),
+FPROP_CASES = [  # (M, N, K) -- ragged M, several tiles in every direction, N an odd
+    (256, 256, 512),    # multiple of 128 (a half-empty 256-wide tile)
     (1000, 384, 640),
     (77, 128, 128),
     (513, 512, 1024),
+    (600, 640, 256),
 ]
 
 
 @pytest.mark.parametrize("M,N,K", FPROP_CASES)
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-def test_fprop_parity(M, N, K, out):
-    _say(f"fprop {M}x{N}x{K} {out}")
+def test_fprop_parity(M, N, K, out, kernel):
+    _say(f"fprop {M}x{N}x{K} {out} {kernel}")
     xb = inputs.random_bits((20, M, K), (M, K), "wide")
     wb = inputs.bf16_bits(oracle.bf16_to_f32(inputs.random_bits((21, N, K), (N, K))) * np.float32(0.02))
     y = run_fprop(xb, wb, out)
@@ -94,8 +102,8 @@ DGRAD_CASES = [(256, 256, 512), (300, 640, 384), (1, 128, 256)]
 
 @pytest.mark.parametrize("M,N,K", DGRAD_CASES)
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-def test_dgrad_parity(M, N, K, out):
-    _say(f"dgrad {M}x{N}x{K} {out}")
+def test_dgrad_parity(M, N, K, out, kernel):
+    _say(f"dgrad {M}x{N}x{K} {out} {kernel}")
     dyb = inputs.student_t((22, M, N), (M, N), 3.0, 1e-3)
     wb = inputs.normal((23, N, K), (N, K), 0.02)
     dx = run_dgrad(dyb, wb, out)
@@ -110,13 +118,27 @@ WGRAD_CASES = [(256, 256, 384), (1024, 384, 256), (128, 128, 128), (2048, 512, 6
 
 
 @pytest.mark.parametrize("M,N,K", WGRAD_CASES)
-def test_wgrad_parity(M, N, K):
-    _say(f"wgrad {M}x{N}x{K}")
+@pytest.mark.parametrize("ws", [None, "auto"])
+def test_wgrad_parity(M, N, K, ws, kernel):
+    _say(f"wgrad {M}x{N}x{K} ws={ws} {kernel}")
     dyb = inputs.student_t((24, M, N), (M, N), 3.0, 1e-3)
     xb = inputs.random_bits((25, M, K), (M, K), "wide")
-    dw = run_wgrad(dyb, xb)
+    dw = run_wgrad(dyb, xb, workspace=ws)
     ref, a, b = ref_wgrad(dyb, xb)
     check_f32(dw, ref, a, b, "wgrad")
+
+
+def test_kernels_agree_with_each_other(monkeypatch):
+    """The two tile shapes sum each block in the same order and fold blocks
+    in the same order, so their FP32 outputs agree to the GEMM tolerance."""
+    M, N, K = 512, 640, 768
+    xb = inputs.random_bits((32,), (M, K), "wide")
+    wb = inputs.normal((33,), (N, K), 0.02)
+    monkeypatch.setenv("FP8BS_GEMM_KERNEL", "small")
+    a = run_fprop(xb, wb, "f32")
+    monkeypatch.setenv("FP8BS_GEMM_KERNEL", "big")
+    b = run_fprop(xb, wb, "f32")
+    assert oracle.rel_frobenius(a, b) < 1e-6
 
 
 def test_wgrad_split_matches_unsplit_bitwise_and_oracle():
@@ -134,7 +156,7 @@ def test_wgrad_split_matches_unsplit_bitwise_and_oracle():
     check_f32(c, ref, da, db, "wgrad unsplit")
 
 
-def test_gemm_special_tiles():
+def test_gemm_special_tiles(kernel):
     """Zero tiles, negative-zero tiles, subnormal-scale tiles and exact E4M3
     grids in both operands."""
     M, N, K = 384, 256, 384
@@ -149,7 +171,7 @@ def test_gemm_special_tiles():
     assert np.all(y[5] == 0)
 
 
-def test_every_code_passes_exactly():
+def test_every_code_passes_exactly(kernel):
     """Rows of A hold all 254 finite codes; B rows are one-hot 1.0 (0x38) with
     unit scales, so C[i][j] = dec(A[i][k_j]) * sA[i] exactly."""
     t = oracle.e4m3_table()
@@ -189,7 +211,7 @@ def test_gemm_empty_and_zero_contraction():
     assert torch.count_nonzero(y).item() == 0
 
 
-def test_gemm_rerun_is_bitwise_identical():
+def test_gemm_rerun_is_bitwise_identical(kernel):
     M, N, K = 640, 512, 1024
     xb = inputs.random_bits((30,), (M, K), "wide")
     wb = inputs.normal((31,), (N, K), 0.02)
