@@ -97,6 +97,9 @@ def parse():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before warmup, run one plain device copy of this many MiB (a "
                          "known-size kernel for scaling HBM byte counters)")
+    ap.add_argument("--quantizer", choices=("fused", "separate"), default="fused",
+                    help="fused: one dual-axis pass per activation/gradient tensor; separate: "
+                         "row-tile and token-axis kernels called one after the other")
     ap.add_argument("--summarize-rocprof", metavar="DIR",
                     help="print a text summary of rocprofv3 CSV output in DIR and exit")
     return ap.parse_args()
@@ -146,27 +149,53 @@ class Plan:
                 nb = int(L.fp8_gemm_wgrad_workspace_bytes(g.M, g.N, g.K))
                 self.ws[g.name] = E((max(nb, 1),), u8) if nb else None
 
-    def ops(self, stream):
+    def ops(self, stream, fused: bool):
         """[(kind, callable, args, algorithmic units)] for one step; units are
-        bytes for quantizers and flops for GEMMs."""
+        bytes for quantizers and flops for GEMMs.  With fused, each activation
+        (forward) and output gradient (backward) is quantized along both axes
+        in one pass; otherwise by the row-tile kernel where its GEMM needs it
+        and by the token-axis kernel before each wgrad."""
         L, cfg = self.L, self.cfg
         ops = []
+
+        def rowtile(name):
+            x = self.act[name]
+            M, K = x.shape
+            q, s = self.rq[name]
+            ops.append(("quant_rowtile", L.fp8_quantize_rowtile,
+                        (x.data_ptr(), M, K, q.data_ptr(), s.data_ptr(), stream),
+                        M * K * 3 + M * (K // 128) * 4))
+
+        def transposed(name):
+            x = self.act[name]
+            M, C = x.shape
+            tq, ts = self.tq[name]
+            ops.append(("quant_transposed", L.fp8_quantize_transposed,
+                        (x.data_ptr(), M, C, tq.data_ptr(), ts.data_ptr(), stream),
+                        M * C * 3 + C * (M // 128) * 4))
+
+        def dual(name):
+            x = self.act[name]
+            M, C = x.shape
+            q, s = self.rq[name]
+            tq, ts = self.tq[name]
+            ops.append(("quant_dual", L.fp8_quantize_dual,
+                        (x.data_ptr(), M, C, q.data_ptr(), s.data_ptr(), tq.data_ptr(),
+                         ts.data_ptr(), stream),
+                        M * C * 4 + M * (C // 128) * 4 + C * (M // 128) * 4))
+
         for layer in range(cfg.layers):
             W = self.w[layer]
             fwd = [g for g in cfg.gemms if g.kind == "fprop"]
             for g in fwd:                                # forward
-                x = self.act[g.a]
-                M, K = x.shape
-                q, s = self.rq[g.a]
-                ops.append(("quant_rowtile", L.fp8_quantize_rowtile,
-                            (x.data_ptr(), M, K, q.data_ptr(), s.data_ptr(), stream),
-                            M * K * 3 + M * (K // 128) * 4))
+                (dual if fused else rowtile)(g.a)
                 w = W[g.b]
                 N, K2 = w.shape
                 wq, wqt, ws = self.wq[g.b]
                 ops.append(("quant_block", L.fp8_quantize_block,
                             (w.data_ptr(), N, K2, wq.data_ptr(), wqt.data_ptr(), ws.data_ptr(),
                              stream), N * K2 * 4 + (N // 128) * (K2 // 128) * 4))
+                q, s = self.rq[g.a]
                 ops.append(("gemm_fprop", L.fp8_gemm_fprop,
                             (q.data_ptr(), s.data_ptr(), wq.data_ptr(), ws.data_ptr(),
                              self.out[g.name].data_ptr(), 1, g.M, g.N, g.K, stream), g.flops))
@@ -174,24 +203,16 @@ class Plan:
                 lin = g.name.split(".")[0]
                 gd = next(x for x in cfg.gemms if x.name == lin + ".dgrad")
                 gw = next(x for x in cfg.gemms if x.name == lin + ".wgrad")
-                dy = self.act[gd.a]
-                M, N = dy.shape
+                (dual if fused else rowtile)(gd.a)
                 dq, ds = self.rq[gd.a]
-                ops.append(("quant_rowtile", L.fp8_quantize_rowtile,
-                            (dy.data_ptr(), M, N, dq.data_ptr(), ds.data_ptr(), stream),
-                            M * N * 3 + M * (N // 128) * 4))
                 wq, wqt, ws = self.wq[gd.b]
                 ops.append(("gemm_dgrad", L.fp8_gemm_dgrad,
                             (dq.data_ptr(), ds.data_ptr(), wqt.data_ptr(), ws.data_ptr(),
                              self.out[gd.name].data_ptr(), 1, gd.M, gd.N, gd.K, stream),
                             gd.flops))
-                for nm in (gw.a, gw.b):
-                    x = self.act[nm]
-                    Mx, C = x.shape
-                    tq, ts = self.tq[nm]
-                    ops.append(("quant_transposed", L.fp8_quantize_transposed,
-                                (x.data_ptr(), Mx, C, tq.data_ptr(), ts.data_ptr(), stream),
-                                Mx * C * 3 + C * (Mx // 128) * 4))
+                if not fused:
+                    transposed(gw.a)
+                    transposed(gw.b)
                 dyt, dyts = self.tq[gw.a]
                 xt, xts = self.tq[gw.b]
                 wsb = self.ws[gw.name]
@@ -201,6 +222,49 @@ class Plan:
                              None if wsb is None else wsb.data_ptr(),
                              0 if wsb is None else wsb.numel(), stream), gw.flops))
         return ops
+
+    def standalone_quant_ops(self, stream):
+        """One row-tile and one token-axis quantization of every shared
+        tensor: the single-axis kernels, timed outside the step when the step
+        uses the fused one."""
+        L = self.L
+        ops = []
+        for name, x in self.act.items():
+            M, C = x.shape
+            q, s = self.rq[name]
+            tq, ts = self.tq[name]
+            ops.append(("quant_rowtile", L.fp8_quantize_rowtile,
+                        (x.data_ptr(), M, C, q.data_ptr(), s.data_ptr(), stream),
+                        M * C * 3 + M * (C // 128) * 4))
+            ops.append(("quant_transposed", L.fp8_quantize_transposed,
+                        (x.data_ptr(), M, C, tq.data_ptr(), ts.data_ptr(), stream),
+                        M * C * 3 + C * (M // 128) * 4))
+        return ops
+
+
+def accumulate_kinds(kinds, ops, events):
+    for i, (kind, _, _, units) in enumerate(ops):
+        ms = events[i].elapsed_time(events[i + 1])
+        k = kinds.setdefault(kind, {"ms": 0.0, "units": 0, "launches": 0})
+        k["ms"] += ms
+        k["units"] += units
+        k["launches"] += 1
+
+
+def kind_summary(kinds, steps):
+    out = {}
+    for kind, k in sorted(kinds.items(), key=lambda kv: -kv[1]["ms"]):
+        sec = k["ms"] / 1e3
+        is_gemm = kind.startswith("gemm")
+        rate = k["units"] / sec / (1e12 if is_gemm else 1e9)
+        peak = PEAK_F16_TFLOPS if is_gemm else PEAK_HBM_GBS
+        out[kind] = {
+            "ms_per_step": round(k["ms"] / steps, 3),
+            "launches_per_step": k["launches"] // steps,
+            "avg_launch_us": round(k["ms"] / k["launches"] * 1e3, 2),
+            "rate": round(rate, 2), "unit": "TFLOP/s" if is_gemm else "GB/s",
+            "frac": round(rate / peak, 4)}
+    return out
 
 
 def run_step(ops, events=None):
@@ -278,7 +342,8 @@ def main():
     fp8.capi()                                   # fails loudly if the library is missing
     plan = Plan(torch, fp8, inputs)
     stream = torch.cuda.current_stream()
-    ops = plan.ops(stream.cuda_stream)
+    fused = args.quantizer == "fused"
+    ops = plan.ops(stream.cuda_stream, fused)
     print(f"# setup: {len(ops)} launches per step, inputs generated in "
           f"{plan.gen_seconds:.1f} s", file=sys.stderr, flush=True)
 
@@ -306,28 +371,21 @@ def main():
     # per-kind device time from the events bracketing every launch
     kinds = {}
     for s in range(args.steps):
-        for i, (kind, _, _, units) in enumerate(ops):
-            ms = events[s][i].elapsed_time(events[s][i + 1])
-            k = kinds.setdefault(kind, {"ms": 0.0, "units": 0, "launches": 0})
-            k["ms"] += ms
-            k["units"] += units
-            k["launches"] += 1
+        accumulate_kinds(kinds, ops, events[s])
+    standalone = {}
+    if fused:
+        sops = plan.standalone_quant_ops(stream.cuda_stream)
+        sev = [torch.cuda.Event(enable_timing=True) for _ in range(len(sops) + 1)]
+        run_step(sops)
+        torch.cuda.synchronize()
+        run_step(sops, sev)
+        torch.cuda.synchronize()
+        accumulate_kinds(standalone, sops, sev)
     step_ms = wall / args.steps * 1e3
     gemm_flops = sum(g.flops for g in plan.cfg.gemms) * plan.cfg.layers
     value = gemm_flops / (wall / args.steps) / 1e12
 
-    breakdown = {}
-    for kind, k in sorted(kinds.items(), key=lambda kv: -kv[1]["ms"]):
-        sec = k["ms"] / 1e3
-        is_gemm = kind.startswith("gemm")
-        rate = k["units"] / sec / (1e12 if is_gemm else 1e9)
-        peak = PEAK_F16_TFLOPS if is_gemm else PEAK_HBM_GBS
-        breakdown[kind] = {
-            "ms_per_step": round(k["ms"] / args.steps, 3),
-            "launches_per_step": k["launches"] // args.steps,
-            "avg_launch_us": round(k["ms"] / k["launches"] * 1e3, 2),
-            "rate": round(rate, 2), "unit": "TFLOP/s" if is_gemm else "GB/s",
-            "frac": round(rate / peak, 4)}
+    breakdown = kind_summary(kinds, args.steps)
     dom = next(iter(breakdown))
     d = breakdown[dom]
     dom_is_gemm = dom.startswith("gemm")
@@ -366,11 +424,13 @@ def main():
                                "4x4096 tokens, hidden 2048, FFN 6144, QKV 4096; per layer "
                                "fprop+dgrad+wgrad of QKV, O, gate/up, down with all quantizers",
                    "tokens": 16384, "layers": 28, "gemm_tflop_per_step": round(gemm_flops / 1e12, 3),
-                   "launches_per_step": len(ops)},
+                   "launches_per_step": len(ops), "quantizer": args.quantizer},
         "pct_fp8_peak": round(100 * value / PEAK_FP8_TFLOPS, 2),
         "roofline": roofline,
         "kernels": breakdown,
     }
+    if standalone:
+        result["kernels_outside_step"] = kind_summary(standalone, 1)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_fraction)
     else:

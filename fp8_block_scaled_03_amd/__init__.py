@@ -7,6 +7,6 @@ Python functions here carry the C names and only marshal arguments.
 """
 from ._binding import (FP8BS_OUT_BF16, FP8BS_OUT_F32, Fp8bsError, capi,  # noqa: F401
                        fp8_encode_e4m3, fp8_gemm_dgrad, fp8_gemm_fprop, fp8_gemm_wgrad,
-                       fp8_gemm_wgrad_workspace_bytes, fp8_quantize_block,
+                       fp8_gemm_wgrad_workspace_bytes, fp8_quantize_block, fp8_quantize_dual,
                        fp8_quantize_rowtile, fp8_quantize_transposed, fp8bs_status_string,
                        fp8bs_version)

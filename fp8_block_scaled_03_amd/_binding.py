@@ -31,6 +31,7 @@ SIGNATURES = {
     "fp8_quantize_rowtile": (_INT, [_P, _I64, _I64, _P, _P, _P]),
     "fp8_quantize_block": (_INT, [_P, _I64, _I64, _P, _P, _P, _P]),
     "fp8_quantize_transposed": (_INT, [_P, _I64, _I64, _P, _P, _P]),
+    "fp8_quantize_dual": (_INT, [_P, _I64, _I64, _P, _P, _P, _P, _P]),
     "fp8_gemm_fprop": (_INT, [_P, _P, _P, _P, _P, _INT, _I64, _I64, _I64, _P]),
     "fp8_gemm_dgrad": (_INT, [_P, _P, _P, _P, _P, _INT, _I64, _I64, _I64, _P]),
     "fp8_gemm_wgrad": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
@@ -142,6 +143,25 @@ def fp8_quantize_transposed(x: torch.Tensor, qt=None, st=None, stream=None):
     _check("fp8_quantize_transposed", capi().fp8_quantize_transposed(
         _ptr(x), M, C, _ptr(qt), _ptr(st), _stream(x, stream)))
     return qt, st
+
+
+def fp8_quantize_dual(x: torch.Tensor, q=None, s=None, qt=None, st=None, stream=None):
+    """x bf16 [M,C] -> (q [M,C], s [M,C/128], qt [C,M], st [C,M/128]) in one pass."""
+    M, C = x.shape
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16")
+    dev = x.device
+    q = torch.empty((M, C), dtype=torch.uint8, device=dev) if q is None else q
+    s = torch.empty((M, C // 128), dtype=torch.float32, device=dev) if s is None else s
+    qt = torch.empty((C, M), dtype=torch.uint8, device=dev) if qt is None else qt
+    st = torch.empty((C, M // 128), dtype=torch.float32, device=dev) if st is None else st
+    _need(q, torch.uint8, (M, C), "q")
+    _need(s, torch.float32, (M, C // 128), "s")
+    _need(qt, torch.uint8, (C, M), "qt")
+    _need(st, torch.float32, (C, M // 128), "st")
+    _check("fp8_quantize_dual", capi().fp8_quantize_dual(
+        _ptr(x), M, C, _ptr(q), _ptr(s), _ptr(qt), _ptr(st), _stream(x, stream)))
+    return q, s, qt, st
 
 
 # ----------------------------------------------------------------------- GEMMs

@@ -119,6 +119,21 @@ fp8bs_status fp8_quantize_transposed(const uint16_t* x, int64_t M, int64_t C, ui
     return launched(fp8bs::launch_quant_transposed(x, M, C, qt, st, stream));
 }
 
+fp8bs_status fp8_quantize_dual(const uint16_t* x, int64_t M, int64_t C, uint8_t* q, float* s,
+                               uint8_t* qt, float* st, fp8bs_stream_t stream) {
+    if (!mult128(M) || !mult128(C)) return FP8BS_ERR_SHAPE;
+    const bool empty = (M == 0 || C == 0);
+    FP8BS_TRY(check_ptr(x, empty, 16));
+    FP8BS_TRY(check_ptr(q, empty, 16));
+    FP8BS_TRY(check_ptr(s, empty, 4));
+    FP8BS_TRY(check_ptr(qt, empty, 16));
+    FP8BS_TRY(check_ptr(st, empty, 4));
+    if (empty) return FP8BS_OK;
+    int cus;
+    FP8BS_TRY(check_device(&cus));
+    return launched(fp8bs::launch_quant_dual(x, M, C, q, s, qt, st, stream));
+}
+
 static fp8bs_status gemm_common(fp8bs::ScaleMode mode, const uint8_t* A, const float* sA,
                                 const uint8_t* B, const float* sB, void* C, int yt, int64_t I,
                                 int64_t J, int64_t Kc, void* workspace, size_t workspace_bytes,

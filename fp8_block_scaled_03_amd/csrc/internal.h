@@ -20,6 +20,8 @@ hipError_t launch_quant_block(const uint16_t* w, int64_t N, int64_t K, uint8_t* 
                               float* s, hipStream_t stream);
 hipError_t launch_quant_transposed(const uint16_t* x, int64_t M, int64_t C, uint8_t* qt, float* st,
                                    hipStream_t stream);
+hipError_t launch_quant_dual(const uint16_t* x, int64_t M, int64_t C, uint8_t* q, float* s,
+                             uint8_t* qt, float* st, hipStream_t stream);
 hipError_t launch_encode_e4m3(const float* x, int64_t n, uint8_t* q, hipStream_t stream);
 
 // C[I, J] = sum_kb sA(i,kb) sB(j,kb) sum_{k in kb} dec(A[i][k]) dec(B[j][k]);

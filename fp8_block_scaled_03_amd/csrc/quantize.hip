@@ -237,6 +237,111 @@ hipError_t launch_quant_transposed(const uint16_t* x, int64_t M, int64_t C, uint
 }
 
 // ---------------------------------------------------------------------------
+// Both axes from one read.  One workgroup per 128 tokens x 128 channels: each
+// token row of the tile is one row tile (1x128 along channels) and each
+// channel column one token-axis tile, so the workgroup reads the BF16 tile
+// once and writes both code sets and both scale sets.
+//   Rows: thread t holds chunk t%16 (8 channels) of rows 16q + t/16, q = 0..7;
+//     the 16 lanes of a row reduce its amax with four lane swaps.
+//   Columns: the tile is copied to LDS with token r stored at physical row
+//     8*(r%16) + r/16 and a 72-dword row stride, so that both the 16-byte row
+//     writes and the column reads below touch 64 distinct banks; thread
+//     (pair p, group g) then reads channels 2p, 2p+1 of tokens 16g .. 16g+15
+//     (two pairs per thread) and reduces each channel over the 8 groups.
+// ---------------------------------------------------------------------------
+constexpr int kDualThreads = 256;
+constexpr int kDualStrideDw = 72;                    // dwords per LDS token row
+
+__device__ __forceinline__ int dual_row(int r) { return ((r & 15) << 3) + (r >> 4); }
+
+__global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t C, uint8_t* __restrict__ q,
+    float* __restrict__ s, uint8_t* __restrict__ qt, float* __restrict__ st) {
+    __shared__ __align__(16) uint32_t tile[kTile * kDualStrideDw];
+    const int tid = threadIdx.x;
+    const int64_t cblocks = C / kTile;
+    const int64_t mb = blockIdx.x / cblocks, cb = blockIdx.x % cblocks;
+    const int64_t m0 = mb * kTile, c0 = cb * kTile;
+    const int chunk = tid & 15;                         // 8 channels: 8*chunk .. +7
+    const int rsub = tid >> 4;                          // rows rsub + 16q
+
+    uint4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        v[i] = load_stream16(x + (m0 + 16 * i + rsub) * C + c0 + chunk * 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = 16 * i + rsub;
+        *reinterpret_cast<uint4*>(tile + dual_row(r) * kDualStrideDw + chunk * 4) = v[i];
+    }
+
+    // Row tiles.
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t m = absmax_fold(absmax_u4(0u, v[i]));
+        m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+        m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+        m = max(m, (uint32_t)__shfl_xor((int)m, 4));
+        m = max(m, (uint32_t)__shfl_xor((int)m, 8));
+        const TileScale ts = tile_scale(m);
+        const int64_t row = m0 + 16 * i + rsub;
+        *reinterpret_cast<uint2*>(q + row * C + c0 + chunk * 8) = quant8(v[i], ts.inv);
+        if (chunk == 0) s[row * cblocks + cb] = ts.s;
+    }
+    __syncthreads();
+
+    // Token-axis tiles.
+    const int g = tid & 7;
+    const int64_t mbn = M / kTile;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int p = (tid >> 3) + 32 * half;           // channel pair: 2p, 2p+1
+        uint32_t d[16];
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            d[i] = tile[dual_row(16 * g + i) * kDualStrideDw + p];
+            m = absmax_pair(m, d[i]);
+        }
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) {
+            uint32_t other = (uint32_t)__shfl_xor((int)m, o);
+            m = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(
+                                                  __builtin_bit_cast(ushort2_t, m),
+                                                  __builtin_bit_cast(ushort2_t, other)));
+        }
+        const TileScale t0 = tile_scale(m & 0xFFFFu);
+        const TileScale t1 = tile_scale(m >> 16);
+        uint32_t w0[4], w1[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t a = d[4 * j], b = d[4 * j + 1], c = d[4 * j + 2], e = d[4 * j + 3];
+            w0[j] = cvt4_e4m3(clamp_e4m3(bf16_lo(a) * t0.inv), clamp_e4m3(bf16_lo(b) * t0.inv),
+                              clamp_e4m3(bf16_lo(c) * t0.inv), clamp_e4m3(bf16_lo(e) * t0.inv));
+            w1[j] = cvt4_e4m3(clamp_e4m3(bf16_hi(a) * t1.inv), clamp_e4m3(bf16_hi(b) * t1.inv),
+                              clamp_e4m3(bf16_hi(c) * t1.inv), clamp_e4m3(bf16_hi(e) * t1.inv));
+        }
+        const int64_t ch = c0 + 2 * p;
+        *reinterpret_cast<uint4*>(qt + ch * M + m0 + g * 16) = make_uint4(w0[0], w0[1], w0[2], w0[3]);
+        *reinterpret_cast<uint4*>(qt + (ch + 1) * M + m0 + g * 16) =
+            make_uint4(w1[0], w1[1], w1[2], w1[3]);
+        if (g == 0) {
+            st[ch * mbn + mb] = t0.s;
+            st[(ch + 1) * mbn + mb] = t1.s;
+        }
+    }
+}
+
+hipError_t launch_quant_dual(const uint16_t* x, int64_t M, int64_t C, uint8_t* q, float* s,
+                             uint8_t* qt, float* st, hipStream_t stream) {
+    int64_t blocks = (M / kTile) * (C / kTile);
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(quant_dual_kernel, dim3((unsigned)blocks), dim3(kDualThreads), 0, stream, x,
+                       M, C, q, s, qt, st);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Diagnostic: clamp + convert, elementwise (4 values per thread).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void encode_e4m3_kernel(const float* __restrict__ x, int64_t n,

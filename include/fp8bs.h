@@ -113,6 +113,20 @@ fp8bs_status fp8_quantize_transposed(const uint16_t* x, int64_t M, int64_t C, ui
                                      float* st, fp8bs_stream_t stream);
 
 /*
+ * Both quantizations of one tensor from a single read: the outputs of
+ * fp8_quantize_rowtile(x) (for fprop or dgrad) and of
+ * fp8_quantize_transposed(x) (for wgrad), bit for bit.  A training step needs
+ * both for every activation and output gradient of a main linear layer
+ * (Puro-2B report, section 2 "FP8"); one pass reads the BF16 tensor once.
+ *   x   bf16 [M, C]
+ *   q   u8   [M, C],  s  f32 [M, C/128]      as fp8_quantize_rowtile
+ *   qt  u8   [C, M],  st f32 [C, M/128]      as fp8_quantize_transposed
+ * M, C >= 0 and multiples of 128.
+ */
+fp8bs_status fp8_quantize_dual(const uint16_t* x, int64_t M, int64_t C, uint8_t* q, float* s,
+                               uint8_t* qt, float* st, fp8bs_stream_t stream);
+
+/*
  * fprop GEMM: Y = X W^T (Puro-2B report, section 2 "FP8": the forward matmul
  * of a main linear layer in FP8).
  *   xq  u8  [M, K],  xs f32 [M, K/128]          from fp8_quantize_rowtile(X)

@@ -30,7 +30,7 @@ def L():
 
 def test_exports_every_header_symbol(L):
     names = header_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -71,6 +71,12 @@ def test_quantizer_argument_errors(L):
     assert L.fp8_quantize_transposed(A16, 128, 96, A16, A16, None) == SHAPE
     assert L.fp8_quantize_transposed(A16, 128, 128, A16, None, None) == NULL
     assert L.fp8_quantize_transposed(None, 0, 0, None, None, None) == OK
+
+    assert L.fp8_quantize_dual(A16, 100, 128, A16, A16, A16, A16, None) == SHAPE
+    assert L.fp8_quantize_dual(A16, 128, 64, A16, A16, A16, A16, None) == SHAPE
+    assert L.fp8_quantize_dual(A16, 128, 128, A16, A16, None, A16, None) == NULL
+    assert L.fp8_quantize_dual(A16, 128, 128, A16, A16, MIS, A16, None) == ALIGN
+    assert L.fp8_quantize_dual(None, 0, 128, None, None, None, None, None) == OK
 
     assert L.fp8_encode_e4m3(A16, -1, A16, None) == SHAPE
     assert L.fp8_encode_e4m3(None, 4, A16, None) == NULL

@@ -166,6 +166,35 @@ def test_transposed_parity_config_tensors(cfg, name):
     _assert_codes(*_transposed_both(bits), what=f"{cfg}.{name}")
 
 
+DUAL_CASES = [("normal", 128, 128), ("wide", 384, 256), ("special", 256, 640), ("wide", 1024, 1024)]
+
+
+def _dual_both(bits):
+    x = to_dev_bf16(bits)
+    q, s, qt, st = fp8.fp8_quantize_dual(x)
+    torch.cuda.synchronize()
+    oq, os_ = oracle.quantize_rowtile(bits)
+    oqt, ost = oracle.quantize_transposed(bits)
+    return (to_np(q), to_np(s), oq, os_), (to_np(qt), to_np(st), oqt, ost)
+
+
+@pytest.mark.parametrize("kind,M,C", DUAL_CASES)
+def test_dual_parity(kind, M, C):
+    bits = inputs.random_bits((12, M, C), (M, C), kind)
+    rows, cols = _dual_both(bits)
+    _assert_codes(*rows, what=f"dual rows {kind} {M}x{C}")
+    _assert_codes(*cols, what=f"dual columns {kind} {M}x{C}")
+
+
+@pytest.mark.parametrize("cfg,name", [("down_bwd", "dY"), ("mlp", "H"), ("qkv", "X")])
+def test_dual_parity_config_tensors(cfg, name):
+    _say(f"dual config {cfg}.{name}")
+    bits = inputs.tensor(cfg, name)
+    rows, cols = _dual_both(bits)
+    _assert_codes(*rows, what=f"dual rows {cfg}.{name}")
+    _assert_codes(*cols, what=f"dual columns {cfg}.{name}")
+
+
 def test_quantizers_are_deterministic():
     bits = inputs.random_bits((11,), (512, 1024), "wide")
     x = to_dev_bf16(bits)
