@@ -7,7 +7,8 @@
 // All three kernels are HBM-bound (read 2 B, write 1 B per element, plus 4 B
 // of scale per tile).  Loads are 16-byte vectors covering whole 128-byte lines,
 // the amax is reduced across the lanes that share a tile, and the codes are
-// produced by the packed FP32 -> E4M3 conversion instruction.
+// produced by the packed FP32 -> E4M3 conversion instruction.  The per-tile
+// divisions are table lookups (see tile_scale in device_common.h).
 #include "device_common.h"
 #include "internal.h"
 
@@ -26,6 +27,8 @@ constexpr int kRowTilesPerBlock = kRowThreads / 8 * kRowUnroll;   // 64
 
 __global__ __launch_bounds__(kRowThreads) void quant_rowtile_kernel(
     const uint4* __restrict__ x, uint2* __restrict__ q, float* __restrict__ s, int64_t ntiles) {
+    __shared__ ScaleTables tab;
+    load_scale_tables(&tab);
     const int sub = threadIdx.x & 7;
     const int64_t base = (int64_t)blockIdx.x * kRowTilesPerBlock + (threadIdx.x >> 3);
     uint4 v[kRowUnroll][2];
@@ -40,6 +43,7 @@ __global__ __launch_bounds__(kRowThreads) void quant_rowtile_kernel(
             v[u][1] = make_uint4(0, 0, 0, 0);
         }
     }
+    __syncthreads();
 #pragma unroll
     for (int u = 0; u < kRowUnroll; ++u) {
         int64_t t = base + u * (kRowThreads / 8);
@@ -48,7 +52,7 @@ __global__ __launch_bounds__(kRowThreads) void quant_rowtile_kernel(
         m = max(m, (uint32_t)__shfl_xor((int)m, 1));
         m = max(m, (uint32_t)__shfl_xor((int)m, 2));
         m = max(m, (uint32_t)__shfl_xor((int)m, 4));
-        TileScale ts = tile_scale(m);
+        TileScale ts = tile_scale(m, &tab);
         if (t < ntiles) {
             q[t * 16 + sub] = quant8(v[u][0], ts.inv);
             q[t * 16 + 8 + sub] = quant8(v[u][1], ts.inv);
@@ -81,6 +85,8 @@ __global__ __launch_bounds__(kBlkThreads) void quant_block_kernel(
     uint8_t* __restrict__ q_t, float* __restrict__ s) {
     __shared__ uint32_t red[kBlkThreads / 64];
     __shared__ __align__(16) uint8_t codes[kTile * kBlkLdsStride];
+    __shared__ ScaleTables tab;
+    load_scale_tables(&tab);
     const int tid = threadIdx.x;
     const int64_t kb_count = K / kTile;
     const int64_t bi = blockIdx.x / kb_count, bj = blockIdx.x % kb_count;
@@ -101,7 +107,7 @@ __global__ __launch_bounds__(kBlkThreads) void quant_block_kernel(
     if ((tid & 63) == 0) red[tid >> 6] = m;
     __syncthreads();
     m = max(max(red[0], red[1]), max(red[2], red[3]));
-    TileScale ts = tile_scale(m);
+    TileScale ts = tile_scale(m, &tab);
     if (tid == 0) s[bi * kb_count + bj] = ts.s;
 
 #pragma unroll
@@ -170,6 +176,8 @@ __global__ __launch_bounds__(kTrThreads) void quant_transposed_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t C, uint8_t* __restrict__ qt,
     float* __restrict__ st) {
     __shared__ uint32_t tile[kTile * kTrStrideDw];
+    __shared__ ScaleTables tab;
+    load_scale_tables(&tab);
     const int tid = threadIdx.x;
     const int64_t cblocks = C / kTrChannels;
     const int64_t mb = blockIdx.x / cblocks, cb = blockIdx.x % cblocks;
@@ -205,16 +213,16 @@ __global__ __launch_bounds__(kTrThreads) void quant_transposed_kernel(
                                               __builtin_bit_cast(ushort2_t, m),
                                               __builtin_bit_cast(ushort2_t, other)));
     }
-    TileScale t0 = tile_scale(m & 0xFFFFu);
-    TileScale t1 = tile_scale(m >> 16);
+    TileScale t0 = tile_scale(m & 0xFFFFu, &tab);
+    TileScale t1 = tile_scale(m >> 16, &tab);
     uint32_t c0w[4], c1w[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         uint32_t a = d[4 * j], b = d[4 * j + 1], c = d[4 * j + 2], e = d[4 * j + 3];
-        c0w[j] = cvt4_e4m3(clamp_e4m3(bf16_lo(a) * t0.inv), clamp_e4m3(bf16_lo(b) * t0.inv),
-                           clamp_e4m3(bf16_lo(c) * t0.inv), clamp_e4m3(bf16_lo(e) * t0.inv));
-        c1w[j] = cvt4_e4m3(clamp_e4m3(bf16_hi(a) * t1.inv), clamp_e4m3(bf16_hi(b) * t1.inv),
-                           clamp_e4m3(bf16_hi(c) * t1.inv), clamp_e4m3(bf16_hi(e) * t1.inv));
+        c0w[j] = cvt4_e4m3(bf16_lo(a) * t0.inv, bf16_lo(b) * t0.inv, bf16_lo(c) * t0.inv,
+                           bf16_lo(e) * t0.inv);
+        c1w[j] = cvt4_e4m3(bf16_hi(a) * t1.inv, bf16_hi(b) * t1.inv, bf16_hi(c) * t1.inv,
+                           bf16_hi(e) * t1.inv);
     }
     const int64_t ch = c0 + 2 * p;
     *reinterpret_cast<uint4*>(qt + ch * M + m0 + g * 16) = make_uint4(c0w[0], c0w[1], c0w[2], c0w[3]);
@@ -258,6 +266,8 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t C, uint8_t* __restrict__ q,
     float* __restrict__ s, uint8_t* __restrict__ qt, float* __restrict__ st) {
     __shared__ __align__(16) uint32_t tile[kTile * kDualStrideDw];
+    __shared__ ScaleTables tab;
+    load_scale_tables(&tab);
     const int tid = threadIdx.x;
     const int64_t cblocks = C / kTile;
     const int64_t mb = blockIdx.x / cblocks, cb = blockIdx.x % cblocks;
@@ -275,6 +285,8 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
         *reinterpret_cast<uint4*>(tile + dual_row(r) * kDualStrideDw + chunk * 4) = v[i];
     }
 
+    __syncthreads();              // scale tables in LDS
+
     // Row tiles.
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -283,7 +295,7 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
         m = max(m, (uint32_t)__shfl_xor((int)m, 2));
         m = max(m, (uint32_t)__shfl_xor((int)m, 4));
         m = max(m, (uint32_t)__shfl_xor((int)m, 8));
-        const TileScale ts = tile_scale(m);
+        const TileScale ts = tile_scale(m, &tab);
         const int64_t row = m0 + 16 * i + rsub;
         *reinterpret_cast<uint2*>(q + row * C + c0 + chunk * 8) = quant8(v[i], ts.inv);
         if (chunk == 0) s[row * cblocks + cb] = ts.s;
@@ -310,16 +322,16 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
                                                   __builtin_bit_cast(ushort2_t, m),
                                                   __builtin_bit_cast(ushort2_t, other)));
         }
-        const TileScale t0 = tile_scale(m & 0xFFFFu);
-        const TileScale t1 = tile_scale(m >> 16);
+        const TileScale t0 = tile_scale(m & 0xFFFFu, &tab);
+        const TileScale t1 = tile_scale(m >> 16, &tab);
         uint32_t w0[4], w1[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const uint32_t a = d[4 * j], b = d[4 * j + 1], c = d[4 * j + 2], e = d[4 * j + 3];
-            w0[j] = cvt4_e4m3(clamp_e4m3(bf16_lo(a) * t0.inv), clamp_e4m3(bf16_lo(b) * t0.inv),
-                              clamp_e4m3(bf16_lo(c) * t0.inv), clamp_e4m3(bf16_lo(e) * t0.inv));
-            w1[j] = cvt4_e4m3(clamp_e4m3(bf16_hi(a) * t1.inv), clamp_e4m3(bf16_hi(b) * t1.inv),
-                              clamp_e4m3(bf16_hi(c) * t1.inv), clamp_e4m3(bf16_hi(e) * t1.inv));
+            w0[j] = cvt4_e4m3(bf16_lo(a) * t0.inv, bf16_lo(b) * t0.inv, bf16_lo(c) * t0.inv,
+                              bf16_lo(e) * t0.inv);
+            w1[j] = cvt4_e4m3(bf16_hi(a) * t1.inv, bf16_hi(b) * t1.inv, bf16_hi(c) * t1.inv,
+                              bf16_hi(e) * t1.inv);
         }
         const int64_t ch = c0 + 2 * p;
         *reinterpret_cast<uint4*>(qt + ch * M + m0 + g * 16) = make_uint4(w0[0], w0[1], w0[2], w0[3]);

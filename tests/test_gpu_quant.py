@@ -211,3 +211,58 @@ def test_empty_quantizer_calls():
     x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
     q, s = fp8.fp8_quantize_rowtile(x)
     assert q.shape == (0, 256) and s.shape == (0, 2)
+
+
+def _every_amax_rows() -> np.ndarray:
+    """[32640, 128] BF16 bits whose row r has amax bit pattern r: every finite
+    non-negative BF16 magnitude (zero, subnormals, the 2^-100 floor and below,
+    all 128 significands at every exponent) is one tile's amax.  With such amax
+    values a = fl(448/a) * a often rounds to 448 (1 + 2^-23), just above 448."""
+    rng = np.random.default_rng(20261203)
+    n = 0x7F80
+    amax = np.arange(n, dtype=np.int64)
+    mags = (rng.random((n, 128)) * (amax[:, None] + 1)).astype(np.int64)     # <= amax
+    pos = rng.integers(0, 128, size=n)
+    mags[np.arange(n), pos] = amax
+    sign = rng.integers(0, 2, size=(n, 128)).astype(np.int64) << 15
+    return (mags | sign).astype(np.uint16)
+
+
+def test_every_bf16_amax_rowtile():
+    _say("rowtile every amax")
+    bits = _every_amax_rows()
+    _assert_codes(*_rowtile_both(bits), what="rowtile every amax")
+
+
+def test_every_bf16_amax_token_axis():
+    _say("transposed every amax")
+    bits = np.ascontiguousarray(_every_amax_rows().T)        # [128, 32640]: columns hold the tiles
+    _assert_codes(*_transposed_both(bits), what="transposed every amax")
+
+
+@pytest.mark.parametrize("orient", ["rows", "columns"])
+def test_every_bf16_amax_dual(orient):
+    _say(f"dual every amax ({orient})")
+    bits = _every_amax_rows()
+    if orient == "columns":
+        bits = np.ascontiguousarray(bits.T)
+    rows, cols = _dual_both(bits)
+    _assert_codes(*rows, what=f"dual rows, every amax ({orient})")
+    _assert_codes(*cols, what=f"dual columns, every amax ({orient})")
+
+
+def test_block_every_significand():
+    # 256 blocks: block b has amax significand b % 128 at one of several exponents
+    rng = np.random.default_rng(77)
+    exps = np.array([27, 1, 60, 120, 127, 128, 180, 254])
+    nb = 256
+    amax = (exps[rng.integers(0, exps.size, size=nb)] << 7) | (np.arange(nb) % 128)
+    bits = np.empty((128, nb * 128), dtype=np.uint16)
+    for b in range(nb):
+        mags = (rng.random((128, 128)) * (amax[b] + 1)).astype(np.int64)
+        mags[rng.integers(0, 128), rng.integers(0, 128)] = amax[b]
+        sign = rng.integers(0, 2, size=(128, 128)).astype(np.int64) << 15
+        bits[:, b * 128:(b + 1) * 128] = (mags | sign).astype(np.uint16)
+    q, qt, s, oq, oqt, os_ = _block_both(bits)
+    _assert_codes(to_np(q), to_np(s), oq, os_, "block every significand")
+    assert np.array_equal(to_np(qt), oqt)
