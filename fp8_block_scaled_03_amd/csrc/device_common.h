@@ -120,11 +120,12 @@ __device__ __forceinline__ uint32_t absmax_u4(uint32_t m, uint4 v) {
     return m;
 }
 
-// FP32 -> BF16 bits, round to nearest, ties to even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+// Two FP32 values -> two BF16 (low half = a), round to nearest, ties to even:
+// one v_cvt_pk_bf16_f32 (the conversion honours the default rounding mode).
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f_t{a, b}, v2bf_t));
 }
 
 }  // namespace fp8bs

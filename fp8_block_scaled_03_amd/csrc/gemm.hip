@@ -223,8 +223,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bs_fp8_kernel(
             if (OUT_BF16) {
                 uint16_t* Cb = reinterpret_cast<uint16_t*>(C);
                 uint2 pk;
-                pk.x = f32_to_bf16_rne(acc[it][jt][0]) | (f32_to_bf16_rne(acc[it][jt][1]) << 16);
-                pk.y = f32_to_bf16_rne(acc[it][jt][2]) | (f32_to_bf16_rne(acc[it][jt][3]) << 16);
+                pk.x = pack_bf16x2(acc[it][jt][0], acc[it][jt][1]);
+                pk.y = pack_bf16x2(acc[it][jt][2], acc[it][jt][3]);
                 *reinterpret_cast<uint2*>(Cb + i * J + j) = pk;
             } else {
                 float* Cf = reinterpret_cast<float*>(C) + (int64_t)blockIdx.y * I * J;
@@ -424,8 +424,8 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
             if (OUT_BF16) {
                 uint16_t* Cb = reinterpret_cast<uint16_t*>(C);
                 uint2 pk;
-                pk.x = f32_to_bf16_rne(acc[it][js][0]) | (f32_to_bf16_rne(acc[it][js][1]) << 16);
-                pk.y = f32_to_bf16_rne(acc[it][js][2]) | (f32_to_bf16_rne(acc[it][js][3]) << 16);
+                pk.x = pack_bf16x2(acc[it][js][0], acc[it][js][1]);
+                pk.y = pack_bf16x2(acc[it][js][2], acc[it][js][3]);
                 *reinterpret_cast<uint2*>(Cb + i * J + j) = pk;
             } else {
                 float* Cf = reinterpret_cast<float*>(C) + (int64_t)blockIdx.y * I * J;

@@ -218,3 +218,43 @@ def test_gemm_rerun_is_bitwise_identical(kernel):
     a = run_fprop(xb, wb, "f32")
     b = run_fprop(xb, wb, "f32")
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 512, 512), (300, 256, 384)])
+def test_bf16_output_is_rne_of_f32_output(M, N, K, kernel):
+    """The BF16 epilogue rounds the same FP32 accumulator the FP32 epilogue
+    stores: bits must equal round-to-nearest-even of the FP32 result."""
+    _say(f"bf16 rounding {M}x{N}x{K} {kernel}")
+    xb = inputs.random_bits((26, M, K), (M, K), "wide")
+    wb = inputs.random_bits((27, N, K), (N, K), "normal")
+    y32 = run_fprop(xb, wb, "f32")
+    y16 = run_fprop(xb, wb, "bf16")
+    want = oracle.f32_to_bf16(y32)
+    bad = np.argwhere(y16 != want)
+    assert bad.size == 0, f"{len(bad)} BF16 outputs differ from RNE(FP32), first {bad[:4].tolist()}"
+
+
+def test_bf16_output_ties_round_to_even(kernel):
+    """Outputs v0(n) + 2^-e(m) v1(n) with E4M3 v0, v1 in [1, 2) and e = 4..9 are
+    exact in FP32 and often fall halfway between two BF16 values; every tile
+    scale is 1 (each tile and block holds a 448)."""
+    M, N, K = 256, 256, 128
+    x = np.zeros((M, K), dtype=np.float32)
+    x[:, 0] = 1.0
+    x[:, 1] = np.exp2(-(4 + np.arange(M) % 6))
+    x[:, 2] = 448.0
+    w = np.zeros((N, K), dtype=np.float32)
+    n = np.arange(N)
+    w[:, 0] = 1.0 + (n % 8) / 8.0
+    w[:, 1] = 1.0 + ((n // 8) % 8) / 8.0
+    w[0, 3] = w[128, 3] = 448.0
+    exact = np.outer(np.ones(M), w[:, 0]) + np.outer(x[:, 1], w[:, 1])
+    assert np.array_equal(exact.astype(np.float32).astype(np.float64), exact)
+    xb, wb = inputs.bf16_bits(x), inputs.bf16_bits(w)
+    y32 = run_fprop(xb, wb, "f32")
+    assert np.array_equal(y32.astype(np.float64), exact), "FP32 result not exact"
+    y16 = run_fprop(xb, wb, "bf16")
+    want = oracle.f32_to_bf16(exact.astype(np.float32))
+    lo = exact.astype(np.float32).view(np.uint32) & 0xFFFF
+    assert (lo == 0x8000).sum() > 1000            # many exact ties
+    assert np.array_equal(y16, want)
