@@ -31,16 +31,36 @@ PEAK_F16_TFLOPS = 2500.0       # MI355X dense FP16 / BF16 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
-    "gemm": os.path.join(ROOT, "fp8_block_scaled_03_amd", "csrc", "gemm.hip"),
-    "quant": os.path.join(ROOT, "fp8_block_scaled_03_amd", "csrc", "quantize.hip"),
+    "gemm": ["gemm.hip", "device_common.h", "internal.h"],
+    "quant": ["quantize.hip", "device_common.h", "internal.h"],
 }
 
 
 def source_digest(kind: str) -> str:
+    """Digest of the sources a kernel kind is built from (counter records
+    taken on other sources are stale)."""
     import hashlib
-    path = KERNEL_SOURCES["gemm" if kind.startswith("gemm") else "quant"]
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for fn in KERNEL_SOURCES["gemm" if kind.startswith("gemm") else "quant"]:
+        with open(os.path.join(ROOT, "fp8_block_scaled_03_amd", "csrc", fn), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_kind(name: str):
+    """(kind, counts_as_call) of a device kernel name: the library call it
+    belongs to, and whether each of its launches is one call of that kind
+    (the split-K reduction is part of a wgrad call, not a call of its own)."""
+    import re
+    if "splitk_reduce_kernel" in name:
+        return "gemm_wgrad", False
+    m = re.search(r"gemm_bs_fp8(?:_big)?_kernel<(\d)", name)
+    if m:
+        return ("gemm_fprop", "gemm_dgrad", "gemm_wgrad")[int(m.group(1))], True
+    for k in ("quant_rowtile", "quant_block", "quant_transposed", "quant_dual"):
+        if k + "_kernel" in name:
+            return k, True
+    return None, False
 
 
 def recorded_traffic(kind: str):
@@ -69,6 +89,17 @@ def summarize_rocprof(d: str) -> None:
             name = r["Name"].split("(")[0].replace("void ", "")[:64]
             print(f"{name:64s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
                   f"{float(r['TotalDurationNs']) / 1e6:10.3f} {float(r['Percentage']):6.2f}")
+        per_kind = {}
+        for r in csv.DictReader(open(path)):
+            kind, is_call = kernel_kind(r["Name"])
+            if kind:
+                k = per_kind.setdefault(kind, [0.0, 0])
+                k[0] += float(r["TotalDurationNs"])
+                k[1] += int(r["Calls"]) if is_call else 0
+        print("# per library call (split-K reductions counted with their wgrad call)")
+        print(f"{'kind':20s} {'calls':>6s} {'avg_us_per_call':>16s} {'total_ms':>10s}")
+        for kind, (ns, calls) in sorted(per_kind.items(), key=lambda kv: -kv[1][0]):
+            print(f"{kind:20s} {calls:6d} {ns / max(calls, 1) / 1e3:16.2f} {ns / 1e6:10.3f}")
     pmc = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
     for path in pmc:
         agg = {}

@@ -66,11 +66,30 @@ __device__ __forceinline__ int lds_off(int row, int c) {
 // vmcnt(0): this wave's global loads (including those into LDS) have landed.
 __device__ __forceinline__ void wait_global_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Output tile of workgroup bid.  Tiles are handed out in groups of
+// kGroupRows tile rows (column-major inside a group) so that workgroups in
+// flight share operand panels; when the tile count is a multiple of 8, the
+// workgroups the dispatcher sends to one XCD (bid % 8) get one contiguous run
+// of that order, so the sharing happens inside one XCD's L2.
+constexpr int kGroupRows = 4;
+
+__device__ __forceinline__ void tile_coords(int bid, int tiles_i, int tiles_j, int* ti, int* tj) {
+    const int T = tiles_i * tiles_j;
+    int t = bid;
+    if ((T & 7) == 0) t = (bid & 7) * (T >> 3) + (bid >> 3);      // contiguous chunk per XCD
+    const int per_group = kGroupRows * tiles_j;
+    const int grp = t / per_group;
+    const int rows = min(kGroupRows, tiles_i - grp * kGroupRows);
+    const int r = t - grp * per_group;
+    *ti = grp * kGroupRows + r % rows;
+    *tj = r / rows;
+}
+
 template <int MODE, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads, 2) void gemm_bs_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
     const float* __restrict__ sB, void* __restrict__ C, int64_t I, int64_t J, int64_t Kc,
-    int tiles_j, int nps) {
+    int tiles_i, int tiles_j, int nps) {
     __shared__ __align__(16) uint8_t As[2][kTileBytes];
     __shared__ __align__(16) uint8_t Bs[2][kTileBytes];
     __shared__ __align__(16) float sAs[2][kBM];
@@ -80,7 +99,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bs_fp8_kernel(
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wi = wave & 1, wj = wave >> 1;
-    const int ti = blockIdx.x / tiles_j, tj = blockIdx.x % tiles_j;
+    int ti, tj;
+    tile_coords(blockIdx.x, tiles_i, tiles_j, &ti, &tj);
     const int64_t i0 = (int64_t)ti * kBM, j0 = (int64_t)tj * kBN;
     const int nkb_all = (int)(Kc / kBK);
     const int kb0 = blockIdx.y * nps;                 // split s: blocks [s*nps, (s+1)*nps)
@@ -252,20 +272,6 @@ constexpr int kBigM = 256;
 constexpr int kBigN = 256;
 constexpr int kBigThreads = 512;
 constexpr int kBigTile = kBigM * kBK;      // one FP8 operand tile: 32 KB
-constexpr int kGroupRows = 4;
-
-__device__ __forceinline__ void tile_coords(int bid, int tiles_i, int tiles_j, int* ti, int* tj) {
-    const int T = tiles_i * tiles_j;
-    int t = bid;
-    if ((T & 7) == 0) t = (bid & 7) * (T >> 3) + (bid >> 3);      // contiguous chunk per XCD
-    const int per_group = kGroupRows * tiles_j;
-    const int grp = t / per_group;
-    const int rows = min(kGroupRows, tiles_i - grp * kGroupRows);
-    const int r = t - grp * per_group;
-    *ti = grp * kGroupRows + r % rows;
-    *tj = r / rows;
-}
-
 template <int MODE, bool OUT_BF16>
 __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
@@ -463,7 +469,8 @@ static hipError_t launch_small(const uint8_t* A, const float* sA, const uint8_t*
     int64_t blocks = tiles_i * tiles_j;
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL((gemm_bs_fp8_kernel<MODE, BF16>), dim3((unsigned)blocks, splits),
-                       dim3(kThreads), 0, stream, A, sA, B, sB, C, I, J, Kc, (int)tiles_j, nps);
+                       dim3(kThreads), 0, stream, A, sA, B, sB, C, I, J, Kc, (int)tiles_i,
+                       (int)tiles_j, nps);
     return hipGetLastError();
 }
 
