@@ -131,6 +131,10 @@ def parse():
     ap.add_argument("--quantizer", choices=("fused", "separate"), default="fused",
                     help="fused: one dual-axis pass per activation/gradient tensor; separate: "
                          "row-tile and token-axis kernels called one after the other")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip the measurements of the layer-level comparisons that follow the "
+                         "step (for profiler runs, whose kernel statistics should hold the step "
+                         "alone)")
     ap.add_argument("--summarize-rocprof", metavar="DIR",
                     help="print a text summary of rocprofv3 CSV output in DIR and exit")
     return ap.parse_args()
@@ -351,6 +355,61 @@ def cpu_baseline(fraction: int):
                       f"rows need; {secs:.1f} s wall"}
 
 
+LAYER_LINEARS = [("qkv", 2048, 4096), ("o", 2048, 2048), ("gate_up", 2048, 12288),
+                 ("down", 6144, 2048)]
+
+
+def _time_events(torch, fn, reps):
+    fn()
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def next_rows(torch, fp8, reps=5):
+    """One decoder layer's four linears at 16,384 tokens, forward + backward:
+    through Fp8Linear (the FP8 block-scaled path) and through torch's BF16
+    linear (the vendor BLAS), on the same shapes."""
+    T = 16384
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    mods, bf_w, xs, dys = [], [], [], []
+    for _, d_in, d_out in LAYER_LINEARS:
+        m = fp8.Fp8Linear(d_in, d_out, device="cuda")
+        mods.append(m)
+        bf_w.append(m.weight.detach().clone().requires_grad_(True))
+        xs.append(torch.randn(T, d_in, device="cuda", generator=gen).bfloat16().requires_grad_(True))
+        dys.append((torch.randn(T, d_out, device="cuda", generator=gen) * 1e-3).bfloat16())
+
+    def fp8_layer():
+        for m, x, dy in zip(mods, xs, dys):
+            x.grad = None
+            m.weight.grad = None
+            m(x).backward(dy)
+
+    def bf16_layer():
+        for w, x, dy in zip(bf_w, xs, dys):
+            x.grad = None
+            w.grad = None
+            torch.nn.functional.linear(x, w).backward(dy)
+
+    flops = sum(3 * 2 * T * d_in * d_out for _, d_in, d_out in LAYER_LINEARS)
+    ms8 = _time_events(torch, fp8_layer, reps)
+    ms16 = _time_events(torch, bf16_layer, reps)
+    return {"f4_fp8_linear_layer": {
+        "workload": "one decoder layer's QKV, O, gate/up and down linears at 16384 tokens, "
+                    "forward + backward (dual quantization of X and dY, block quantization of "
+                    "W, fprop, dgrad, wgrad)",
+        "fp8_ms": round(ms8, 3), "fp8_tflops": round(flops / ms8 / 1e9, 1),
+        "torch_bf16_ms": round(ms16, 3), "torch_bf16_tflops": round(flops / ms16 / 1e9, 1),
+        "fp8_speedup_vs_torch_bf16": round(ms16 / ms8, 3)}}
+
+
 def main():
     args = parse()
     if args.summarize_rocprof:
@@ -462,6 +521,10 @@ def main():
     }
     if standalone:
         result["kernels_outside_step"] = kind_summary(standalone, 1)
+    if not args.no_next_rows:
+        del plan, ops, events
+        torch.cuda.empty_cache()
+        result["next_rows"] = next_rows(torch, fp8)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_fraction)
     else:

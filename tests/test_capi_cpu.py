@@ -126,3 +126,16 @@ def test_product_path_never_imports_the_oracle():
                 src = open(os.path.join(dirpath, fn)).read()
                 assert "import oracle" not in src and "from oracle" not in src, fn
                 assert "fp8bs_oracle" not in src, fn
+
+
+def test_fp8_linear_has_no_cpu_path():
+    """The layer runs only through the device library: CPU tensors are refused
+    before any call, there is no host fallback."""
+    import torch
+
+    import fp8_block_scaled_03_amd as pkg
+    lin = pkg.Fp8Linear(256, 128)
+    with pytest.raises(ValueError):
+        lin(torch.randn(128, 256).bfloat16())
+    with pytest.raises(ValueError):
+        pkg.Fp8Linear(200, 128)
