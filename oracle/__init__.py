@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_quantize_transposed.argtypes = [P, i64, i64, P, P, ctypes.c_int]
         L.oracle_gemm.restype = ctypes.c_int
         L.oracle_gemm.argtypes = [ctypes.c_int, P, P, P, P, i64, i64, i64, P, i64, P, ctypes.c_int]
+        L.oracle_gemm_bf16.restype = ctypes.c_int
+        L.oracle_gemm_bf16.argtypes = [P, P, i64, i64, i64, P, i64, P, ctypes.c_int]
         L.oracle_version.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -191,6 +193,26 @@ def gemm_dgrad(dyq, dys, wq_t, ws, rows=None, threads: int = 0):
 def gemm_wgrad(dytq, dyts, xtq, xts, rows=None, threads: int = 0):
     """dW[N,K] = dY^T X from dytq [N,M], dyts [N,M/128], xtq [K,M], xts [K,M/128]."""
     return gemm(MODE_ROW, dytq, dyts, xtq, xts, rows, threads)
+
+
+def gemm_bf16(a_bits: np.ndarray, b_bits: np.ndarray, rows=None, threads: int = 0) -> np.ndarray:
+    """Unquantized comparator: out [I or len(rows), J] float32 = A B^T for BF16
+    bit patterns A [I,K], B [J,K]; products exact, sum in float64, one rounding."""
+    A = _u16(a_bits)
+    B = _u16(b_bits)
+    I, K = A.shape
+    J, K2 = B.shape
+    if K2 != K:
+        raise ValueError("contraction lengths differ")
+    r = None
+    n = I
+    if rows is not None:
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n = r.size
+    out = np.empty((n, J), dtype=np.float32)
+    _check(lib().oracle_gemm_bf16(_ptr(A), _ptr(B), I, J, K, _ptr(r), n, _ptr(out), threads),
+           "gemm_bf16")
+    return out
 
 
 # ----------------------------------------------------------------------- metrics

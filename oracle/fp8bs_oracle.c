@@ -328,3 +328,42 @@ int oracle_gemm(int mode, const uint8_t* A, const float* sA, const uint8_t* B, c
     free(Bu);
     return status;
 }
+
+/* ------------------------------------------------------------------------- */
+/* BF16 GEMM, the unquantized comparator of the FP8 path (the report weighs   */
+/* its FP8 training against BF16 training of the same model):                 */
+/*     out[i][j] = sum_k a(i,k) * b(j,k),  a = A [I,K], b = B [J,K] BF16 bits. */
+/* A product of two BF16 values has at most 16 significant bits and is exact  */
+/* in double; the sum runs in double, k ascending, and is rounded once to     */
+/* FP32.  rows (nullable) lists the output rows; out is [nrows][J].            */
+/* ------------------------------------------------------------------------- */
+int oracle_gemm_bf16(const uint16_t* A, const uint16_t* B, int64_t I, int64_t J, int64_t K,
+                     const int64_t* rows, int64_t nrows, float* out, int threads) {
+    if (I < 0 || J < 0 || K < 0) return ORACLE_ERR_SHAPE;
+    if (!rows) nrows = I;
+    for (int64_t r = 0; rows && r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= I) return ORACLE_ERR_ARG;
+    for (int64_t e = 0; e < J * K; ++e)
+        if (!isfinite(bf16_to_f32(B[e]))) return ORACLE_ERR_NONFINITE;
+    int status = ORACLE_OK;
+    set_threads(threads);
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t i = rows ? rows[r] : r;
+        int row_bad = 0;
+        for (int64_t k = 0; k < K; ++k)
+            if (!isfinite(bf16_to_f32(A[i * K + k]))) row_bad = 1;
+        if (row_bad) {
+            #pragma omp atomic write
+            status = ORACLE_ERR_NONFINITE;
+            continue;
+        }
+        for (int64_t j = 0; j < J; ++j) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += (double)bf16_to_f32(A[i * K + k]) * (double)bf16_to_f32(B[j * K + k]);
+            out[r * J + j] = (float)acc;
+        }
+    }
+    return status;
+}
