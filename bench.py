@@ -31,7 +31,7 @@ PEAK_F16_TFLOPS = 2500.0       # MI355X dense FP16 / BF16 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
-    "gemm": ["gemm.hip", "device_common.h", "internal.h"],
+    "gemm": ["gemm.hip", "gemm_common.h", "device_common.h", "internal.h"],
     "quant": ["quantize.hip", "device_common.h", "internal.h"],
 }
 
@@ -372,6 +372,39 @@ def _time_events(torch, fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
+def bf16_comparison(torch, fp8, cfg, fp8_ms_per_layer, reps=5):
+    """The 12 GEMMs of one layer in TN form on BF16 operands: this library's
+    BF16 kernel and torch's BF16 matmul (the vendor BLAS), against the FP8
+    GEMMs' device time per layer in the step."""
+    gen = torch.Generator(device="cuda").manual_seed(1)
+    own = blas = 0.0
+    flops = 0
+    for g in cfg.gemms:
+        if g.kind == "fprop":
+            I, J, K = g.M, g.N, g.K
+        elif g.kind == "dgrad":
+            I, J, K = g.M, g.K, g.N
+        else:
+            I, J, K = g.N, g.K, g.M
+        out = torch.float32 if g.kind == "wgrad" else torch.bfloat16
+        a = torch.randn(I, K, device="cuda", generator=gen).bfloat16()
+        b = torch.randn(J, K, device="cuda", generator=gen).bfloat16()
+        c = torch.empty(I, J, device="cuda", dtype=out)
+        own += _time_events(torch, lambda: fp8.bf16_gemm_tn(a, b, out_dtype=out, c=c), reps)
+        blas += _time_events(torch, lambda: torch.matmul(a, b.t(), out=c) if out == torch.bfloat16
+                             else torch.matmul(a, b.t()), reps)
+        flops += g.flops
+        del a, b, c
+    return {"f2_bf16_gemm": {
+        "workload": "one layer's 12 GEMMs of the linear set (16384 tokens) in TN form on BF16 "
+                    "operands, FP32 accumulation, BF16 out (FP32 for wgrad)",
+        "bf16_ms_per_layer": round(own, 3), "bf16_tflops": round(flops / own / 1e9, 1),
+        "fp8_ms_per_layer": round(fp8_ms_per_layer, 3),
+        "fp8_tflops": round(flops / fp8_ms_per_layer / 1e9, 1),
+        "fp8_speedup_vs_own_bf16": round(own / fp8_ms_per_layer, 3),
+        "torch_bf16_ms_per_layer": round(blas, 3), "torch_bf16_tflops": round(flops / blas / 1e9, 1)}}
+
+
 def next_rows(torch, fp8, reps=5):
     """One decoder layer's four linears at 16,384 tokens, forward + backward:
     through Fp8Linear (the FP8 block-scaled path) and through torch's BF16
@@ -522,9 +555,13 @@ def main():
     if standalone:
         result["kernels_outside_step"] = kind_summary(standalone, 1)
     if not args.no_next_rows:
+        cfg_obj, cfg_layers = plan.cfg, plan.cfg.layers
         del plan, ops, events
         torch.cuda.empty_cache()
-        result["next_rows"] = next_rows(torch, fp8)
+        fp8_gemm_ms = sum(v["ms_per_step"] for k, v in breakdown.items()
+                          if k.startswith("gemm")) / cfg_layers
+        result["next_rows"] = {**bf16_comparison(torch, fp8, cfg_obj, fp8_gemm_ms),
+                               **next_rows(torch, fp8)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_fraction)
     else:

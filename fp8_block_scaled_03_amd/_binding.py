@@ -36,6 +36,7 @@ SIGNATURES = {
     "fp8_gemm_dgrad": (_INT, [_P, _P, _P, _P, _P, _INT, _I64, _I64, _I64, _P]),
     "fp8_gemm_wgrad": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
     "fp8_gemm_wgrad_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64]),
+    "bf16_gemm_tn": (_INT, [_P, _P, _P, _INT, _I64, _I64, _I64, _P]),
     "fp8_encode_e4m3": (_INT, [_P, _I64, _P, _P]),
     "fp8bs_status_string": (ctypes.c_char_p, [_INT]),
     "fp8bs_version": (_INT, []),
@@ -222,6 +223,21 @@ def fp8_gemm_wgrad(dytq, dyts, xtq, xts, dw=None, workspace=None, stream=None):
         _ptr(dytq), _ptr(dyts), _ptr(xtq), _ptr(xts), _ptr(dw), M, N, K, ws_ptr, ws_bytes,
         _stream(dytq, stream)))
     return dw
+
+
+def bf16_gemm_tn(a: torch.Tensor, b: torch.Tensor, out_dtype=torch.bfloat16, c=None, stream=None):
+    """C [I,J] = A B^T for BF16 A [I,K], B [J,K] (the unquantized comparator)."""
+    if a.dtype != torch.bfloat16 or b.dtype != torch.bfloat16:
+        raise ValueError("a and b must be bfloat16")
+    I, K = a.shape
+    J = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("contraction lengths differ")
+    code = _dtype_code(out_dtype)
+    c = _out((I, J), code, a.device, c)
+    _check("bf16_gemm_tn", capi().bf16_gemm_tn(_bits16(a).data_ptr(), _bits16(b).data_ptr(),
+                                               _ptr(c), code, I, J, K, _stream(a, stream)))
+    return c
 
 
 def fp8_encode_e4m3(x: torch.Tensor, q=None, stream=None):

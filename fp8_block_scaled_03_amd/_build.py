@@ -8,7 +8,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfp8bs.so")
-SOURCES = ["quantize.hip", "gemm.hip", "capi.cpp"]
+SOURCES = ["quantize.hip", "gemm.hip", "gemm_bf16.hip", "capi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

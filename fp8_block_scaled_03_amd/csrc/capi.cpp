@@ -190,6 +190,21 @@ size_t fp8_gemm_wgrad_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     return fp8bs::gemm_workspace_bytes(fp8bs::kScaleRow, N, K, M, cus);
 }
 
+fp8bs_status bf16_gemm_tn(const uint16_t* a, const uint16_t* b, void* c, fp8bs_out_dtype ct,
+                          int64_t I, int64_t J, int64_t K, fp8bs_stream_t stream) {
+    if (I < 0 || !mult128(J) || !mult128(K)) return FP8BS_ERR_SHAPE;
+    if ((int)ct != FP8BS_OUT_F32 && (int)ct != FP8BS_OUT_BF16) return FP8BS_ERR_DTYPE;
+    const bool out_empty = (I == 0 || J == 0);
+    const bool in_empty = out_empty || K == 0;
+    FP8BS_TRY(check_ptr(a, in_empty, 16));
+    FP8BS_TRY(check_ptr(b, in_empty, 16));
+    FP8BS_TRY(check_ptr(c, out_empty, 16));
+    if (out_empty) return FP8BS_OK;
+    int cus;
+    FP8BS_TRY(check_device(&cus));
+    return launched(fp8bs::launch_gemm_bf16(a, b, c, ct == FP8BS_OUT_BF16, I, J, K, stream));
+}
+
 fp8bs_status fp8_encode_e4m3(const float* x, int64_t n, uint8_t* q, fp8bs_stream_t stream) {
     if (n < 0) return FP8BS_ERR_SHAPE;
     FP8BS_TRY(check_ptr(x, n == 0, 16));

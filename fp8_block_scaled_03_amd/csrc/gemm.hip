@@ -30,11 +30,11 @@
 #include <cstring>
 
 #include "device_common.h"
+#include "gemm_common.h"
 #include "internal.h"
 
 namespace fp8bs {
 
-typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
@@ -52,38 +52,6 @@ constexpr int kBN = 128;
 constexpr int kBK = 128;
 constexpr int kThreads = 256;
 constexpr int kTileBytes = kBM * kBK;       // one FP8 operand tile: 16 KB
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Byte offset of 16-byte chunk c (0..7, K = 16c .. 16c+15) of tile row r.  The
-// chunk index is XORed with bits 1..3 of the row, so that the 16 lanes served
-// together by a 16-byte LDS read (16 consecutive rows, one logical chunk)
-// cover all 64 banks exactly once.
-__device__ __forceinline__ int lds_off(int row, int c) {
-    return row * kBK + ((c ^ ((row >> 1) & 7)) << 4);
-}
-
-// vmcnt(0): this wave's global loads (including those into LDS) have landed.
-__device__ __forceinline__ void wait_global_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// Output tile of workgroup bid.  Tiles are handed out in groups of
-// kGroupRows tile rows (column-major inside a group) so that workgroups in
-// flight share operand panels; when the tile count is a multiple of 8, the
-// workgroups the dispatcher sends to one XCD (bid % 8) get one contiguous run
-// of that order, so the sharing happens inside one XCD's L2.
-constexpr int kGroupRows = 4;
-
-__device__ __forceinline__ void tile_coords(int bid, int tiles_i, int tiles_j, int* ti, int* tj) {
-    const int T = tiles_i * tiles_j;
-    int t = bid;
-    if ((T & 7) == 0) t = (bid & 7) * (T >> 3) + (bid >> 3);      // contiguous chunk per XCD
-    const int per_group = kGroupRows * tiles_j;
-    const int grp = t / per_group;
-    const int rows = min(kGroupRows, tiles_i - grp * kGroupRows);
-    const int r = t - grp * per_group;
-    *ti = grp * kGroupRows + r % rows;
-    *tj = r / rows;
-}
 
 template <int MODE, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads, 2) void gemm_bs_fp8_kernel(

@@ -33,4 +33,8 @@ hipError_t launch_gemm(ScaleMode mode, const uint8_t* A, const float* sA, const 
 
 size_t gemm_workspace_bytes(ScaleMode mode, int64_t I, int64_t J, int64_t Kc, int num_cus);
 
+// C[I, J] = A B^T with A [I, K], B [J, K] BF16 (unquantized comparator).
+hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* B, void* C, bool out_bf16,
+                            int64_t I, int64_t J, int64_t K, hipStream_t stream);
+
 }  // namespace fp8bs

@@ -177,6 +177,19 @@ fp8bs_status fp8_gemm_wgrad(const uint8_t* dytq, const float* dyts, const uint8_
 size_t fp8_gemm_wgrad_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
+ * Unquantized comparator (Puro-2B technical report, section 2 "FP8": FP8
+ * training is weighed against BF16 training of the same model):
+ *   C[I,J] = A B^T,  A bf16 [I,K], B bf16 [J,K] (contraction contiguous),
+ * products accumulated in FP32, C BF16 (RNE) or FP32 [I,J] per ct.
+ * Any of the three linear-layer GEMMs is this form once its operands are laid
+ * out with the contraction contiguous.  I >= 0; J and K positive multiples of
+ * 128 (FP8BS_ERR_SHAPE otherwise; J or K = 0 allowed as empty).  All pointers
+ * 16-byte aligned device pointers; caller-owned; asynchronous on stream.
+ */
+fp8bs_status bf16_gemm_tn(const uint16_t* a, const uint16_t* b, void* c, fp8bs_out_dtype ct,
+                          int64_t I, int64_t J, int64_t K, fp8bs_stream_t stream);
+
+/*
  * Diagnostic: the quantizers' FP32 -> E4M3 step on its own, elementwise:
  * q[i] = E4M3 round-to-nearest-even of clamp(x[i], -448, 448).  Lets a test
  * sweep the device conversion over any set of FP32 values.

@@ -18,7 +18,7 @@ OK, NULL, SHAPE, ALIGN, DTYPE = 0, 1, 2, 3, 4
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fp8\w*)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:fp8|bf16)\w*)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -30,7 +30,7 @@ def L():
 
 def test_exports_every_header_symbol(L):
     names = header_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -110,6 +110,18 @@ def test_gemm_argument_errors(L):
     assert w(None, None, None, None, None, 128, 0, 128, None, 0, None) == OK
     assert L.fp8_gemm_wgrad_workspace_bytes(100, 128, 128) == 0
     assert L.fp8_gemm_wgrad_workspace_bytes(-128, 128, 128) == 0
+
+
+def test_bf16_gemm_argument_errors(L):
+    f = L.bf16_gemm_tn
+    assert f(A16, A16, A16, 1, 4, 100, 128, None) == SHAPE
+    assert f(A16, A16, A16, 1, 4, 128, 96, None) == SHAPE
+    assert f(A16, A16, A16, 1, -1, 128, 128, None) == SHAPE
+    assert f(A16, A16, A16, 5, 4, 128, 128, None) == DTYPE
+    assert f(None, A16, A16, 1, 4, 128, 128, None) == NULL
+    assert f(A16, MIS, A16, 1, 4, 128, 128, None) == ALIGN
+    assert f(A16, A16, A16 + 8, 0, 4, 128, 128, None) == ALIGN
+    assert f(None, None, None, 1, 0, 128, 128, None) == OK
 
 
 def test_binding_names_match_c_names():
