@@ -405,6 +405,41 @@ def bf16_comparison(torch, fp8, cfg, fp8_ms_per_layer, reps=5):
         "torch_bf16_ms_per_layer": round(blas, 3), "torch_bf16_tflops": round(flops / blas / 1e9, 1)}}
 
 
+def dgrad_epilogue_quantization(torch, fp8, cfg, reps=5):
+    """One layer's four dgrad GEMMs at 16,384 tokens: dgrad with BF16 output
+    followed by the row-tile quantizer on dX, against the same with the
+    quantizer fused into the dgrad epilogue (BF16 dX kept, or codes only)."""
+    gen = torch.Generator(device="cuda").manual_seed(2)
+    sep = fused = codes_only = 0.0
+    for g in cfg.gemms:
+        if g.kind != "dgrad":
+            continue
+        dy = (torch.randn(g.M, g.N, device="cuda", generator=gen) * 1e-3).bfloat16()
+        w = (torch.randn(g.N, g.K, device="cuda", generator=gen) * 0.02).bfloat16()
+        dyq, dys = fp8.fp8_quantize_rowtile(dy)
+        _, wqt, ws = fp8.fp8_quantize_block(w)
+        dx = torch.empty(g.M, g.K, device="cuda", dtype=torch.bfloat16)
+        q = torch.empty(g.M, g.K, device="cuda", dtype=torch.uint8)
+        s = torch.empty(g.M, g.K // 128, device="cuda", dtype=torch.float32)
+
+        def separate():
+            fp8.fp8_gemm_dgrad(dyq, dys, wqt, ws, dx=dx)
+            fp8.fp8_quantize_rowtile(dx, q, s)
+
+        sep += _time_events(torch, separate, reps)
+        fused += _time_events(torch, lambda: fp8.fp8_gemm_dgrad_quantized(
+            dyq, dys, wqt, ws, dx=dx, dxq=q, dxs=s), reps)
+        codes_only += _time_events(torch, lambda: fp8.fp8_gemm_dgrad_quantized(
+            dyq, dys, wqt, ws, with_bf16=False, dxq=q, dxs=s), reps)
+        del dy, w, dyq, dys, wqt, ws, dx, q, s
+    return {"f3_dgrad_quantize_on_produce": {
+        "workload": "one layer's four dgrad GEMMs of the linear set (16384 tokens), each "
+                    "followed by 1x128 row-tile quantization of dX",
+        "separate_ms_per_layer": round(sep, 3), "fused_ms_per_layer": round(fused, 3),
+        "fused_codes_only_ms_per_layer": round(codes_only, 3),
+        "fused_speedup": round(sep / fused, 3)}}
+
+
 def next_rows(torch, fp8, reps=5):
     """One decoder layer's four linears at 16,384 tokens, forward + backward:
     through Fp8Linear (the FP8 block-scaled path) and through torch's BF16
@@ -561,6 +596,7 @@ def main():
         fp8_gemm_ms = sum(v["ms_per_step"] for k, v in breakdown.items()
                           if k.startswith("gemm")) / cfg_layers
         result["next_rows"] = {**bf16_comparison(torch, fp8, cfg_obj, fp8_gemm_ms),
+                               **dgrad_epilogue_quantization(torch, fp8, cfg_obj),
                                **next_rows(torch, fp8)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_fraction)

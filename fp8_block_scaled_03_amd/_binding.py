@@ -34,6 +34,7 @@ SIGNATURES = {
     "fp8_quantize_dual": (_INT, [_P, _I64, _I64, _P, _P, _P, _P, _P]),
     "fp8_gemm_fprop": (_INT, [_P, _P, _P, _P, _P, _INT, _I64, _I64, _I64, _P]),
     "fp8_gemm_dgrad": (_INT, [_P, _P, _P, _P, _P, _INT, _I64, _I64, _I64, _P]),
+    "fp8_gemm_dgrad_quantized": (_INT, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "fp8_gemm_wgrad": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
     "fp8_gemm_wgrad_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64]),
     "bf16_gemm_tn": (_INT, [_P, _P, _P, _INT, _I64, _I64, _I64, _P]),
@@ -202,6 +203,27 @@ def fp8_gemm_dgrad(dyq, dys, wq_t, ws, out_dtype=torch.bfloat16, dx=None, stream
     _check("fp8_gemm_dgrad", capi().fp8_gemm_dgrad(
         _ptr(dyq), _ptr(dys), _ptr(wq_t), _ptr(ws), _ptr(dx), code, M, N, K, _stream(dyq, stream)))
     return dx
+
+
+def fp8_gemm_dgrad_quantized(dyq, dys, wq_t, ws, with_bf16=True, dx=None, dxq=None, dxs=None,
+                             stream=None):
+    """dgrad with its BF16 output quantized in 1x128 row tiles in the epilogue:
+    returns (dx bf16 [M,K] or None, dxq uint8 [M,K], dxs float32 [M,K/128])."""
+    M, N = dyq.shape
+    K = wq_t.shape[0]
+    dev = dyq.device
+    if with_bf16 and dx is None:
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    if dx is not None:
+        _need(dx, torch.bfloat16, (M, K), "dx")
+    dxq = torch.empty((M, K), dtype=torch.uint8, device=dev) if dxq is None else dxq
+    dxs = torch.empty((M, K // 128), dtype=torch.float32, device=dev) if dxs is None else dxs
+    _need(dxq, torch.uint8, (M, K), "dxq")
+    _need(dxs, torch.float32, (M, K // 128), "dxs")
+    _check("fp8_gemm_dgrad_quantized", capi().fp8_gemm_dgrad_quantized(
+        _ptr(dyq), _ptr(dys), _ptr(wq_t), _ptr(ws), _ptr(dx), _ptr(dxq), _ptr(dxs), M, N, K,
+        _stream(dyq, stream)))
+    return dx, dxq, dxs
 
 
 def fp8_gemm_wgrad_workspace_bytes(M: int, N: int, K: int) -> int:

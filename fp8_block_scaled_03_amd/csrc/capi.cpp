@@ -174,6 +174,27 @@ fp8bs_status fp8_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t*
                        stream);
 }
 
+fp8bs_status fp8_gemm_dgrad_quantized(const uint8_t* dyq, const float* dys, const uint8_t* wq_t,
+                                      const float* ws, uint16_t* dx, uint8_t* dxq, float* dxs,
+                                      int64_t M, int64_t N, int64_t K, fp8bs_stream_t stream) {
+    if (M < 0 || !mult128(N) || !mult128(K)) return FP8BS_ERR_SHAPE;
+    const bool out_empty = (M == 0 || K == 0);
+    const bool in_empty = out_empty || N == 0;
+    FP8BS_TRY(check_ptr(dyq, in_empty, 16));
+    FP8BS_TRY(check_ptr(dys, in_empty, 4));
+    FP8BS_TRY(check_ptr(wq_t, in_empty, 16));
+    FP8BS_TRY(check_ptr(ws, in_empty, 4));
+    FP8BS_TRY(check_ptr(dxq, out_empty, 16));
+    FP8BS_TRY(check_ptr(dxs, out_empty, 4));
+    if (dx && !aligned(dx, 16)) return FP8BS_ERR_ALIGN;
+    if (out_empty) return FP8BS_OK;
+    int cus;
+    FP8BS_TRY(check_device(&cus));
+    // TN form, as fp8_gemm_dgrad: rows of dY against rows of W^T, contraction N.
+    return launched(fp8bs::launch_gemm_quantized(fp8bs::kScaleBlockT, dyq, dys, wq_t, ws, dx, dxq,
+                                                 dxs, M, K, N, stream));
+}
+
 fp8bs_status fp8_gemm_wgrad(const uint8_t* dytq, const float* dyts, const uint8_t* xtq,
                             const float* xts, float* dw, int64_t M, int64_t N, int64_t K,
                             void* workspace, size_t workspace_bytes, fp8bs_stream_t stream) {

@@ -240,11 +240,16 @@ constexpr int kBigM = 256;
 constexpr int kBigN = 256;
 constexpr int kBigThreads = 512;
 constexpr int kBigTile = kBigM * kBK;      // one FP8 operand tile: 32 KB
-template <int MODE, bool OUT_BF16>
+// QOUT: the epilogue also quantizes the BF16 output in 1x128 row tiles (the
+// rule of quant_rowtile_kernel) and stores codes Cq [I, J] and scales
+// Cs [I, J/128]; C (BF16) may then be null.  A wave's 128 output columns of a
+// row are exactly one such tile, held by the four lanes r16 + 16g.
+template <int MODE, bool OUT_BF16, bool QOUT = false>
 __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
     const float* __restrict__ sB, void* __restrict__ C, int64_t I, int64_t J, int64_t Kc,
-    int tiles_i, int tiles_j, int nps) {
+    int tiles_i, int tiles_j, int nps, uint8_t* __restrict__ Cq = nullptr,
+    float* __restrict__ Cs = nullptr) {
     __shared__ __align__(16) uint8_t As[2][kBigTile];
     __shared__ __align__(16) uint8_t Bs[2][kBigTile];
     __shared__ __align__(16) float sAs[2][kBigM];
@@ -388,6 +393,38 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
 
     // epilogue: lane owns C[i][j .. j+3]; split s writes its own FP32 slice
     if (j0 + 128 * wj >= J) return;
+    if constexpr (QOUT) {
+        const int64_t jt = j0 + 128 * wj;                  // first column of the row tiles
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int64_t i = i0 + wi * 64 + it * 16 + r16;
+            uint32_t pk[8][2];
+            uint32_t m = 0;
+#pragma unroll
+            for (int js = 0; js < 8; ++js) {
+                pk[js][0] = pack_bf16x2(acc[it][js][0], acc[it][js][1]);
+                pk[js][1] = pack_bf16x2(acc[it][js][2], acc[it][js][3]);
+                m = absmax_pair(absmax_pair(m, pk[js][0]), pk[js][1]);
+            }
+            m = absmax_fold(m);
+            m = max(m, (uint32_t)__shfl_xor((int)m, 16));
+            m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+            const TileScale ts = tile_scale(m, &g_scale_tables);
+            if (i >= I) continue;
+#pragma unroll
+            for (int js = 0; js < 8; ++js) {
+                const int64_t j = jt + js * 16 + 4 * g;
+                if (C)
+                    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(C) + i * J + j) =
+                        make_uint2(pk[js][0], pk[js][1]);
+                *reinterpret_cast<uint32_t*>(Cq + i * J + j) =
+                    cvt4_e4m3(bf16_lo(pk[js][0]) * ts.inv, bf16_hi(pk[js][0]) * ts.inv,
+                              bf16_lo(pk[js][1]) * ts.inv, bf16_hi(pk[js][1]) * ts.inv);
+            }
+            if (g == 0) Cs[i * (J / kTile) + jt / kTile] = ts.s;
+        }
+        return;
+    }
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int64_t i = i0 + wi * 64 + it * 16 + r16;
@@ -532,6 +569,26 @@ static hipError_t launch_mode(const uint8_t* A, const float* sA, const uint8_t* 
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0,
                        stream, reinterpret_cast<const float4*>(workspace),
                        reinterpret_cast<float4*>(C), n4, p.splits);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_quantized(ScaleMode mode, const uint8_t* A, const float* sA,
+                                 const uint8_t* B, const float* sB, uint16_t* C, uint8_t* Cq,
+                                 float* Cs, int64_t I, int64_t J, int64_t Kc, hipStream_t stream) {
+    const int tiles_i = (int)((I + kBigM - 1) / kBigM);
+    const int tiles_j = (int)((J + kBigN - 1) / kBigN);
+    const int nkb = (int)(Kc / kBK);
+    if (tiles_i == 0 || tiles_j == 0) return hipSuccess;
+    if (mode == kScaleBlockT)
+        hipLaunchKernelGGL((gemm_bs_fp8_big_kernel<kScaleBlockT, true, true>),
+                           dim3(tiles_i * tiles_j, 1), dim3(kBigThreads), 0, stream, A, sA, B, sB,
+                           (void*)C, I, J, Kc, tiles_i, tiles_j, nkb, Cq, Cs);
+    else if (mode == kScaleBlock)
+        hipLaunchKernelGGL((gemm_bs_fp8_big_kernel<kScaleBlock, true, true>),
+                           dim3(tiles_i * tiles_j, 1), dim3(kBigThreads), 0, stream, A, sA, B, sB,
+                           (void*)C, I, J, Kc, tiles_i, tiles_j, nkb, Cq, Cs);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -33,6 +33,13 @@ hipError_t launch_gemm(ScaleMode mode, const uint8_t* A, const float* sA, const 
 
 size_t gemm_workspace_bytes(ScaleMode mode, int64_t I, int64_t J, int64_t Kc, int num_cus);
 
+// As launch_gemm with BF16 output (C, nullable), plus the output quantized in
+// 1x128 row tiles: codes Cq [I, J], scales Cs [I, J/128].  Modes kScaleBlock
+// and kScaleBlockT; 256x256 kernel, no split.
+hipError_t launch_gemm_quantized(ScaleMode mode, const uint8_t* A, const float* sA,
+                                 const uint8_t* B, const float* sB, uint16_t* C, uint8_t* Cq,
+                                 float* Cs, int64_t I, int64_t J, int64_t Kc, hipStream_t stream);
+
 // C[I, J] = A B^T with A [I, K], B [J, K] BF16 (unquantized comparator).
 hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* B, void* C, bool out_bf16,
                             int64_t I, int64_t J, int64_t K, hipStream_t stream);

@@ -177,6 +177,23 @@ fp8bs_status fp8_gemm_wgrad(const uint8_t* dytq, const float* dyts, const uint8_
 size_t fp8_gemm_wgrad_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
+ * dgrad with its output quantized as it is produced (the row-tile quantizer
+ * fused into the GEMM epilogue; Puro-2B technical report, section 2 "FP8":
+ * BF16 work next to the FP8 matmuls then needs no separate pass over dX to
+ * feed an FP8 GEMM).  dX = dY W exactly as fp8_gemm_dgrad computes it, rounded
+ * to BF16 (RNE); the BF16 values are then quantized in 1x128 row tiles along
+ * K by the rule of fp8_quantize_rowtile, so the codes and scales equal
+ * fp8_quantize_rowtile applied to the BF16 dX bit for bit.
+ *   dyq, dys, wq_t, ws as fp8_gemm_dgrad; dx bf16 [M,K] or NULL (then only
+ *   the codes are written); dxq e4m3 [M,K]; dxs f32 [M,K/128].
+ * Shapes and errors as fp8_gemm_dgrad (dxq, dy/w pointers 16-byte aligned,
+ * scales 4-byte aligned).  Always the 256x256 tile kernel, no split.
+ */
+fp8bs_status fp8_gemm_dgrad_quantized(const uint8_t* dyq, const float* dys, const uint8_t* wq_t,
+                                      const float* ws, uint16_t* dx, uint8_t* dxq, float* dxs,
+                                      int64_t M, int64_t N, int64_t K, fp8bs_stream_t stream);
+
+/*
  * Unquantized comparator (Puro-2B technical report, section 2 "FP8": FP8
  * training is weighed against BF16 training of the same model):
  *   C[I,J] = A B^T,  A bf16 [I,K], B bf16 [J,K] (contraction contiguous),

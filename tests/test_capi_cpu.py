@@ -30,7 +30,7 @@ def L():
 
 def test_exports_every_header_symbol(L):
     names = header_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -110,6 +110,17 @@ def test_gemm_argument_errors(L):
     assert w(None, None, None, None, None, 128, 0, 128, None, 0, None) == OK
     assert L.fp8_gemm_wgrad_workspace_bytes(100, 128, 128) == 0
     assert L.fp8_gemm_wgrad_workspace_bytes(-128, 128, 128) == 0
+
+
+def test_dgrad_quantized_argument_errors(L):
+    f = L.fp8_gemm_dgrad_quantized
+    assert f(A16, A16, A16, A16, A16, A16, A16, 4, 100, 128, None) == SHAPE
+    assert f(A16, A16, A16, A16, A16, A16, A16, 4, 128, 96, None) == SHAPE
+    assert f(A16, A16, A16, A16, None, None, A16, 4, 128, 128, None) == NULL
+    assert f(A16, A16, A16, A16, None, A16, None, 4, 128, 128, None) == NULL
+    assert f(A16, A16, A16, A16, A16 + 2, A16, A16, 4, 128, 128, None) == ALIGN
+    assert f(A16, A16, A16, A16, None, MIS, A16, 4, 128, 128, None) == ALIGN
+    assert f(None, None, None, None, None, None, None, 0, 128, 128, None) == OK
 
 
 def test_bf16_gemm_argument_errors(L):
