@@ -18,14 +18,24 @@
 // block in FP32, which is folded into the FP32 accumulator with one FMA per
 // output element (acc += P * sA*sB).
 //
-// Workgroup tile 128 (i) x 128 (j) x 128 (k), four waves in a 2x2 grid, each
-// wave a 64x64 patch of 4x4 MFMA tiles; two workgroups share a CU.  Each
-// thread loads its share of the next block's FP8 codes into registers while
-// the current block is contracted; the codes are widened to FP16 once, as
-// they are stored to LDS (16-byte chunks XOR-swizzled by row so the fragment
-// reads are bank-conflict free).  The MFMA operands are swapped (B tile as
-// the first source) so that each lane owns four consecutive output columns of
-// one row and stores them as one vector.
+// Two kernels share that arithmetic:
+//   gemm_bs_fp8_kernel      workgroup tile 128 (i) x 128 (j) x 128 (k), four
+//                           waves of 64x64, two workgroups per CU; used for
+//                           wgrad (two per-row scales per fold) and for grids
+//                           too small to give every CU a 256x256 tile; can
+//                           split the contraction (FP32 slices in a caller
+//                           workspace, summed in a fixed order).
+//   gemm_bs_fp8_big_kernel  256 x 256 x 128, eight waves of 64x128, one
+//                           workgroup per CU; fprop and dgrad.  Each wave
+//                           widens its A fragments once per block and keeps
+//                           them in registers while B fragments stream.
+// Both stage the FP8 tiles of the next block in LDS with direct global->LDS
+// loads (double buffered, 16-byte chunks XOR-swizzled by row so the fragment
+// reads are bank-conflict free) while the current block is contracted, and
+// hand out output tiles in an XCD-aware grouped order (gemm_common.h).  The
+// MFMA operands are swapped (B fragment as the first source) so that each
+// lane owns four consecutive output columns of one row and stores them as one
+// vector.
 #include <cstdlib>
 #include <cstring>
 
@@ -269,18 +279,14 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
     const int nkb_row = nkb_all;                  // scale row stride (blocks per row)
     const int64_t jb_count = J / kBN;             // 128-wide column blocks of B
 
-    // Direct global -> LDS loads: wave w fills 1 KB pieces 4w .. 4w+3 of each
-    // 32 KB tile (8 rows each), lane l landing at row 8*piece + l/8, physical
-    // chunk l%8 of the swizzle.
-    const uint8_t* a_src[4];
-    const uint8_t* b_src[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        int row = 8 * (4 * wave + j) + (lane >> 3);
-        int c = (lane & 7) ^ ((row >> 1) & 7);
-        a_src[j] = A + min(i0 + row, I - 1) * Kc + c * 16;
-        b_src[j] = B + min(j0 + row, J - 1) * Kc + c * 16;
-    }
+    // Direct global -> LDS loads.  Waves 0..3 fill the 32 KB A and B tiles
+    // (wave w: 1 KB pieces 8w .. 8w+7, 8 rows each; lane l lands at row
+    // 8*piece + l/8, physical chunk l%8 of the swizzle); waves 4..7, which
+    // share SIMDs with them, only load scales and go straight on to their
+    // MFMAs after each barrier.  For this lane, piece 8w + j is row
+    // prow + 8j with swizzled chunk pc (j even) or pc ^ 4 (j odd).
+    const int prow = 64 * (wave & 3) + (lane >> 3);
+    const int pc = (lane & 7) ^ ((prow >> 1) & 7);
     // Scales: waves 0..3 load the A-row scales of rows 64w + lane, waves 4..7
     // the B scales of rows 64(w-4) + lane (per row, or their column block's).
     const float* s_src;
@@ -304,12 +310,22 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
 
     auto issue_loads = [&](int kb, int buf) {
         const int64_t koff = (int64_t)kb * kBK;
+        if (wave < 4) {
+            // Recomputed per call (the empty asm hides the loop invariance):
+            // sixteen precomputed 64-bit addresses would cost 32 registers.
+            int pr = prow, pcc = pc;
+            asm volatile("" : "+v"(pr), "+v"(pcc));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            __builtin_amdgcn_global_load_lds(a_src[j] + koff,
-                                             (lds_void*)(&As[buf][(4 * wave + j) * 1024]), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(b_src[j] + koff,
-                                             (lds_void*)(&Bs[buf][(4 * wave + j) * 1024]), 16, 0, 0);
+            for (int j = 0; j < 8; ++j) {
+                const int row = pr + 8 * j;
+                const int c = (j & 1) ? (pcc ^ 4) : pcc;
+                __builtin_amdgcn_global_load_lds(A + min(i0 + row, I - 1) * Kc + koff + c * 16,
+                                                 (lds_void*)(&As[buf][(8 * wave + j) * 1024]), 16,
+                                                 0, 0);
+                __builtin_amdgcn_global_load_lds(B + min(j0 + row, J - 1) * Kc + koff + c * 16,
+                                                 (lds_void*)(&Bs[buf][(8 * wave + j) * 1024]), 16,
+                                                 0, 0);
+            }
         }
         float* sdst = (wave < 4) ? &sAs[buf][64 * wave] : &sBs[buf][64 * (wave - 4)];
         __builtin_amdgcn_global_load_lds(s_src + kb * s_step, (lds_void*)sdst, 4, 0, 0);

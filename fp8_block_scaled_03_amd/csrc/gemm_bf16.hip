@@ -45,28 +45,28 @@ __global__ __launch_bounds__(kB16Threads, 1) void gemm_bf16_kernel(
     const int nks = (int)(K / kB16K);
     const int64_t row_bytes = K * 2;
 
-    // Direct global -> LDS loads: wave w fills 1 KB pieces 4w .. 4w+3 of each
-    // tile (8 rows each); lane l lands at row 8*piece + l/8, physical chunk
-    // l%8, and fetches the logical chunk the swizzle puts there.  Rows past
-    // the end of A or B are clamped to the last row (never stored).
-    const uint8_t* a_blk = reinterpret_cast<const uint8_t*>(A) + i0 * row_bytes;
-    const uint8_t* b_blk = reinterpret_cast<const uint8_t*>(B) + j0 * row_bytes;
-    int64_t a_off[4], b_off[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int row = 8 * (4 * wave + j) + (lane >> 3);
-        const int c = (lane & 7) ^ ((row >> 1) & 7);
-        a_off[j] = (min(i0 + row, I - 1) - i0) * row_bytes + c * 16;
-        b_off[j] = (min(j0 + row, J - 1) - j0) * row_bytes + c * 16;
-    }
+    // Direct global -> LDS loads.  Waves 0..3 fill both 32 KB tiles (wave w:
+    // 1 KB pieces 8w .. 8w+7, 8 rows each; lane l lands at row 8*piece + l/8,
+    // physical chunk l%8, and fetches the logical chunk the swizzle puts
+    // there); waves 4..7 go straight on to their MFMAs after each barrier.
+    // Rows past the end of A or B are clamped to the last row (never stored).
+    const uint8_t* a_bytes = reinterpret_cast<const uint8_t*>(A);
+    const uint8_t* b_bytes = reinterpret_cast<const uint8_t*>(B);
+    const int prow = 64 * (wave & 3) + (lane >> 3);
+    const int pc = (lane & 7) ^ ((prow >> 1) & 7);
     auto issue_loads = [&](int ks, int buf) {
+        if (wave >= 4) return;
         const int64_t koff = (int64_t)ks * kRowBytes;
+        int pr = prow, pcc = pc;
+        asm volatile("" : "+v"(pr), "+v"(pcc));       // keep the address math per call
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            __builtin_amdgcn_global_load_lds(a_blk + koff + a_off[j],
-                                             (lds_void*)(&As[buf][(4 * wave + j) * 1024]), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(b_blk + koff + b_off[j],
-                                             (lds_void*)(&Bs[buf][(4 * wave + j) * 1024]), 16, 0, 0);
+        for (int j = 0; j < 8; ++j) {
+            const int row = pr + 8 * j;
+            const int c = (j & 1) ? (pcc ^ 4) : pcc;    // row + 8j flips bit 2 of the swizzle for odd j
+            __builtin_amdgcn_global_load_lds(a_bytes + min(i0 + row, I - 1) * row_bytes + koff + c * 16,
+                                             (lds_void*)(&As[buf][(8 * wave + j) * 1024]), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(b_bytes + min(j0 + row, J - 1) * row_bytes + koff + c * 16,
+                                             (lds_void*)(&Bs[buf][(8 * wave + j) * 1024]), 16, 0, 0);
         }
     };
 
