@@ -534,21 +534,30 @@ static Plan plan_gemm(ScaleMode mode, int64_t I, int64_t J, int64_t Kc, int num_
     if (nkb == 0) return p;
     const int64_t big_tiles = ((I + kBigM - 1) / kBigM) * ((J + kBigN - 1) / kBigN);
     const int64_t small_tiles = ((I + kBM - 1) / kBM) * (J / kBN);
-    // fprop/dgrad: the 256x256 tile once it gives every CU a tile.  wgrad (two
-    // per-row scales, so two VALU operations per output in the fold): the
-    // 128x128 tile, whose lighter register use suits that fold better.
+    // fprop/dgrad: the 256x256 tile once it gives every CU a tile.  wgrad: the
+    // 128x128 tile (measured in the full training step, it edges out the
+    // 256x256 one, whose splits move more FP32 partials through HBM).
     if (force == 2) p.big = true;
     else if (force == 1) p.big = false;
     else p.big = (mode != kScaleRow) && I >= kBigM && big_tiles >= cus;
-    // Split the contraction when the tiles cannot fill the CUs twice over
-    // (FP32 output only, with a caller workspace).
+    // Split the contraction (FP32 output only, with a caller workspace) into
+    // s = 1, 2, 4, ... parts, taking the s that minimizes (full waves of
+    // resident workgroups) x (contraction blocks per workgroup); ties go to
+    // the smaller s, whose reduction pass is cheaper.
     if (mode == kScaleRow && allow_split) {
         const int64_t tiles = p.big ? big_tiles : small_tiles;
-        const int64_t target = p.big ? 2 * cus : 4 * cus;     // workgroups in flight: 1 or 2 per CU
-        int s = 1;
-        while (tiles * s < target && nkb / (2 * s) >= 4) s *= 2;
-        if (s > 1) {
-            p.nps = (int)((nkb + s - 1) / s);
+        const int64_t slots = p.big ? cus : 2 * cus;           // workgroups resident at once
+        int best = 1;
+        int64_t best_cost = -1;
+        for (int s = 1; s <= 16 && nkb / s >= 4; s *= 2) {
+            const int64_t cost = ((tiles * s + slots - 1) / slots) * ((nkb + s - 1) / s);
+            if (best_cost < 0 || cost < best_cost) {
+                best_cost = cost;
+                best = s;
+            }
+        }
+        if (best > 1) {
+            p.nps = (int)((nkb + best - 1) / best);
             p.splits = (int)((nkb + p.nps - 1) / p.nps);
         }
     }
