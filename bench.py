@@ -123,7 +123,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle leg (for profiler runs)")
-    ap.add_argument("--cpu-fraction", type=int, default=16,
+    ap.add_argument("--cpu-fraction", type=int, default=6,
                     help="the CPU sample computes 1/N of layer 0's output rows")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before warmup, run one plain device copy of this many MiB (a "
