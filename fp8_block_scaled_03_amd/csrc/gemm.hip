@@ -535,11 +535,12 @@ static Plan plan_gemm(ScaleMode mode, int64_t I, int64_t J, int64_t Kc, int num_
     const int64_t big_tiles = ((I + kBigM - 1) / kBigM) * ((J + kBigN - 1) / kBigN);
     const int64_t small_tiles = ((I + kBM - 1) / kBM) * (J / kBN);
     // fprop/dgrad: the 256x256 tile once it gives every CU a tile.  wgrad: the
-    // 128x128 tile (measured in the full training step, it edges out the
-    // 256x256 one, whose splits move more FP32 partials through HBM).
+    // 256x256 tile (with a split of the contraction) while its tiles alone
+    // cannot fill the CUs; past that, the 128x128 tile, which needs no split
+    // and so moves no FP32 partials through HBM (measured in the full step).
     if (force == 2) p.big = true;
     else if (force == 1) p.big = false;
-    else p.big = (mode != kScaleRow) && I >= kBigM && big_tiles >= cus;
+    else p.big = I >= kBigM && (mode == kScaleRow ? big_tiles < cus : big_tiles >= cus);
     // Split the contraction (FP32 output only, with a caller workspace) into
     // s = 1, 2, 4, ... parts, taking the s that minimizes (full waves of
     // resident workgroups) x (contraction blocks per workgroup); ties go to
