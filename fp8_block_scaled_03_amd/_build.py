@@ -19,7 +19,7 @@ FLAGS = [
     "-shared",
     "-fno-fast-math",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
-    # keep the compiler from forming packed FP32 instructions (see the build notes)
+    # scalar FP32 only: the compiler may not form packed FP32 instructions (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
     "-Wno-unused-command-line-argument",
