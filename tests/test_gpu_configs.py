@@ -1,8 +1,10 @@
-"""GPU parity at the full Qwen3-1.7B-like configurations, launched exactly as
-the benchmark launches them, compared with the oracle on sampled output rows
-(row tiles and weight blocks are local, so the oracle quantizes only what the
-sampled rows need).  Quantizer outputs of these tensors are compared in full
-by test_gpu_quant."""
+"""GPU parity at the full Qwen3-1.7B-like configurations, launched as the
+benchmark launches them (activations and gradients through the dual-axis
+quantizer, weights through the block quantizer, wgrad with its split-K
+workspace), compared with the oracle on sampled output rows (row tiles and
+weight blocks are local, so the oracle quantizes only what the sampled rows
+need).  Quantizer outputs of these tensors are compared in full by
+test_gpu_quant."""
 import numpy as np
 import pytest
 import torch
@@ -30,7 +32,7 @@ def gemm_case(kind, abits, bbits, out, rows, dev_cache=None):
     dgrad and dY [M, N] for wgrad (rows then index dW's rows = dY channels)."""
     a, b = to_dev_bf16(abits), to_dev_bf16(bbits)
     if kind == "fprop":
-        aq, as_ = fp8.fp8_quantize_rowtile(a)
+        aq, as_, _, _ = fp8.fp8_quantize_dual(a)
         bq, _, bs = fp8.fp8_quantize_block(b, with_transpose=False)
         y = fp8.fp8_gemm_fprop(aq, as_, bq, bs, out_dtype=out)
         torch.cuda.synchronize()
@@ -40,7 +42,7 @@ def gemm_case(kind, abits, bbits, out, rows, dev_cache=None):
         ref = oracle.gemm_fprop(oq, os_, wq, ws)
         ad, bd = oracle.dequantize_rows(oq, os_), oracle.dequantize_block(wq, ws)
     elif kind == "dgrad":
-        aq, as_ = fp8.fp8_quantize_rowtile(a)
+        aq, as_, _, _ = fp8.fp8_quantize_dual(a)
         _, bqt, bs = fp8.fp8_quantize_block(b)
         y = fp8.fp8_gemm_dgrad(aq, as_, bqt, bs, out_dtype=out)
         torch.cuda.synchronize()
@@ -50,8 +52,8 @@ def gemm_case(kind, abits, bbits, out, rows, dev_cache=None):
         ref = oracle.gemm_dgrad(oq, os_, wqt, ws)
         ad, bd = oracle.dequantize_rows(oq, os_), oracle.dequantize_block(wq, ws).T
     else:
-        atq, ats = fp8.fp8_quantize_transposed(a)
-        btq, bts = fp8.fp8_quantize_transposed(b)
+        _, _, atq, ats = fp8.fp8_quantize_dual(a)
+        _, _, btq, bts = fp8.fp8_quantize_dual(b)
         y = fp8.fp8_gemm_wgrad(atq, ats, btq, bts, workspace="auto")
         torch.cuda.synchronize()
         got = to_np(y)[rows]
