@@ -576,7 +576,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3",
+        "dtype": "e4m3 operands on f16 mfma, f32 accumulation",
         "data": "synthetic",
         "config": {"workload": "linear_set: 28-layer Qwen3-1.7B-like decoder micro-batch, "
                                "4x4096 tokens, hidden 2048, FFN 6144, QKV 4096; per layer "

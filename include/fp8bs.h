@@ -38,10 +38,10 @@
  *   - Threads: calls are re-entrant and may be made from several host threads
  *     as long as their output buffers do not overlap.
  *   - Kernel choice: the GEMMs pick a 256x256 or a 128x128 workgroup tile by
- *     size; the environment variable FP8BS_GEMM_KERNEL=small|big (read at each
- *     call)
- *     forces one of them, for testing both at any size.  Results agree to the
- *     GEMM tolerance either way.
+ *     shape (and, for wgrad, a split of the contraction); the environment
+ *     variable FP8BS_GEMM_KERNEL=small|big, read at each call, forces one of
+ *     them, for testing both at any size.  Results agree to the GEMM
+ *     tolerance either way.
  */
 #ifndef FP8BS_H
 #define FP8BS_H
