@@ -57,6 +57,8 @@ def kernel_kind(name: str):
     m = re.search(r"gemm_bs_fp8(?:_big)?_kernel<(\d)", name)
     if m:
         return ("gemm_fprop", "gemm_dgrad", "gemm_wgrad")[int(m.group(1))], True
+    if "quant_dual_kernel<false>" in name:          # the token-axis-only instance
+        return "quant_transposed", True
     for k in ("quant_rowtile", "quant_block", "quant_transposed", "quant_dual"):
         if k + "_kernel" in name:
             return k, True

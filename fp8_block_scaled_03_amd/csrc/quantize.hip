@@ -162,93 +162,12 @@ hipError_t launch_quant_block(const uint16_t* w, int64_t N, int64_t K, uint8_t* 
 }
 
 // ---------------------------------------------------------------------------
-// Token-axis tiles.  One workgroup per 128 tokens x 64 channels.  The BF16
-// tile is staged in LDS (rows of 64 channels, padded to 33 dwords); thread
-// (pair p, group g) then owns channels 2p, 2p+1 of tokens 16g .. 16g+15, so
-// the 8 threads of a channel pair reduce the amax with three lane swaps and
-// each writes 16 contiguous codes per channel to the transposed output.
-// ---------------------------------------------------------------------------
-constexpr int kTrThreads = 256;
-constexpr int kTrChannels = 64;
-constexpr int kTrStrideDw = kTrChannels / 2 + 1;   // 33 dwords per token row
-
-__global__ __launch_bounds__(kTrThreads) void quant_transposed_kernel(
-    const uint16_t* __restrict__ x, int64_t M, int64_t C, uint8_t* __restrict__ qt,
-    float* __restrict__ st) {
-    __shared__ uint32_t tile[kTile * kTrStrideDw];
-    __shared__ ScaleTables tab;
-    load_scale_tables(&tab);
-    const int tid = threadIdx.x;
-    const int64_t cblocks = C / kTrChannels;
-    const int64_t mb = blockIdx.x / cblocks, cb = blockIdx.x % cblocks;
-    const int64_t m0 = mb * kTile, c0 = cb * kTrChannels;
-
-    // Load: 8 threads per token row (16 bytes each), 32 rows per pass.
-#pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-        int row = pass * 32 + (tid >> 3), chunk = tid & 7;
-        uint4 v = load_stream16(x + (m0 + row) * C + c0 + chunk * 8);
-        uint32_t* dst = tile + row * kTrStrideDw + chunk * 4;
-        dst[0] = v.x;
-        dst[1] = v.y;
-        dst[2] = v.z;
-        dst[3] = v.w;
-    }
-    __syncthreads();
-
-    const int g = tid & 7;          // token group: tokens 16g .. 16g+15
-    const int p = tid >> 3;         // channel pair: channels 2p, 2p+1
-    uint32_t d[16];
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        d[i] = tile[(g * 16 + i) * kTrStrideDw + p];
-        m = absmax_pair(m, d[i]);
-    }
-    // m holds (channel 2p in the low half, channel 2p+1 in the high half)
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
-        uint32_t other = (uint32_t)__shfl_xor((int)m, o);
-        m = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(
-                                              __builtin_bit_cast(ushort2_t, m),
-                                              __builtin_bit_cast(ushort2_t, other)));
-    }
-    TileScale t0 = tile_scale(m & 0xFFFFu, &tab);
-    TileScale t1 = tile_scale(m >> 16, &tab);
-    uint32_t c0w[4], c1w[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        uint32_t a = d[4 * j], b = d[4 * j + 1], c = d[4 * j + 2], e = d[4 * j + 3];
-        c0w[j] = cvt4_e4m3(bf16_lo(a) * t0.inv, bf16_lo(b) * t0.inv, bf16_lo(c) * t0.inv,
-                           bf16_lo(e) * t0.inv);
-        c1w[j] = cvt4_e4m3(bf16_hi(a) * t1.inv, bf16_hi(b) * t1.inv, bf16_hi(c) * t1.inv,
-                           bf16_hi(e) * t1.inv);
-    }
-    const int64_t ch = c0 + 2 * p;
-    *reinterpret_cast<uint4*>(qt + ch * M + m0 + g * 16) = make_uint4(c0w[0], c0w[1], c0w[2], c0w[3]);
-    *reinterpret_cast<uint4*>(qt + (ch + 1) * M + m0 + g * 16) =
-        make_uint4(c1w[0], c1w[1], c1w[2], c1w[3]);
-    if (g == 0) {
-        const int64_t mbn = M / kTile;
-        st[ch * mbn + mb] = t0.s;
-        st[(ch + 1) * mbn + mb] = t1.s;
-    }
-}
-
-hipError_t launch_quant_transposed(const uint16_t* x, int64_t M, int64_t C, uint8_t* qt, float* st,
-                                   hipStream_t stream) {
-    int64_t blocks = (M / kTile) * (C / kTrChannels);
-    if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(quant_transposed_kernel, dim3((unsigned)blocks), dim3(kTrThreads), 0, stream,
-                       x, M, C, qt, st);
-    return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// Both axes from one read.  One workgroup per 128 tokens x 128 channels: each
-// token row of the tile is one row tile (1x128 along channels) and each
-// channel column one token-axis tile, so the workgroup reads the BF16 tile
-// once and writes both code sets and both scale sets.
+// Token-axis tiles, alone or with the row tiles from the same read.  One
+// workgroup per 128 tokens x 128 channels: each channel column of the tile is
+// one token-axis tile and each token row one row tile (1x128 along channels),
+// so with ROWS the workgroup reads the BF16 tile once and writes both code
+// sets and both scale sets (fp8_quantize_dual); without, only the token-axis
+// ones (fp8_quantize_transposed).
 //   Rows: thread t holds chunk t%16 (8 channels) of rows 16q + t/16, q = 0..7;
 //     the 16 lanes of a row reduce its amax with four lane swaps.
 //   Columns: the tile is copied to LDS with token r stored at physical row
@@ -262,6 +181,7 @@ constexpr int kDualStrideDw = 72;                    // dwords per LDS token row
 
 __device__ __forceinline__ int dual_row(int r) { return ((r & 15) << 3) + (r >> 4); }
 
+template <bool ROWS>
 __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t C, uint8_t* __restrict__ q,
     float* __restrict__ s, uint8_t* __restrict__ qt, float* __restrict__ st) {
@@ -289,7 +209,7 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
 
     // Row tiles.
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 8 && ROWS; ++i) {
         uint32_t m = absmax_fold(absmax_u4(0u, v[i]));
         m = max(m, (uint32_t)__shfl_xor((int)m, 1));
         m = max(m, (uint32_t)__shfl_xor((int)m, 2));
@@ -344,12 +264,21 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
     }
 }
 
+hipError_t launch_quant_transposed(const uint16_t* x, int64_t M, int64_t C, uint8_t* qt, float* st,
+                                   hipStream_t stream) {
+    int64_t blocks = (M / kTile) * (C / kTile);
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(quant_dual_kernel<false>, dim3((unsigned)blocks), dim3(kDualThreads), 0,
+                       stream, x, M, C, (uint8_t*)nullptr, (float*)nullptr, qt, st);
+    return hipGetLastError();
+}
+
 hipError_t launch_quant_dual(const uint16_t* x, int64_t M, int64_t C, uint8_t* q, float* s,
                              uint8_t* qt, float* st, hipStream_t stream) {
     int64_t blocks = (M / kTile) * (C / kTile);
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(quant_dual_kernel, dim3((unsigned)blocks), dim3(kDualThreads), 0, stream, x,
-                       M, C, q, s, qt, st);
+    hipLaunchKernelGGL(quant_dual_kernel<true>, dim3((unsigned)blocks), dim3(kDualThreads), 0, stream,
+                       x, M, C, q, s, qt, st);
     return hipGetLastError();
 }
 
