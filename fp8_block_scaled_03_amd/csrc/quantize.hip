@@ -4,8 +4,9 @@
 // DeepSeek-V3-style fine-grained quantization -- 1x128 tiles for activations
 // and gradients, 128x128 blocks for weights, one FP32 scale per tile.
 //
-// All three kernels are HBM-bound (read 2 B, write 1 B per element, plus 4 B
-// of scale per tile).  Loads are 16-byte vectors covering whole 128-byte lines,
+// The kernels are HBM-bound (read 2 B and write 1 B per element per output
+// axis, plus 4 B of scale per tile): row tiles, weight blocks, and token-axis
+// tiles with or without the row tiles of the same read.  Loads are 16-byte vectors covering whole 128-byte lines,
 // the amax is reduced across the lanes that share a tile, and the codes are
 // produced by the packed FP32 -> E4M3 conversion instruction.  The per-tile
 // divisions are table lookups (see tile_scale in device_common.h).
