@@ -442,7 +442,7 @@ def dgrad_epilogue_quantization(torch, fp8, cfg, reps=5):
         "fused_speedup": round(sep / fused, 3)}}
 
 
-def next_rows(torch, fp8, reps=5):
+def fp8_linear_comparison(torch, fp8, reps=5):
     """One decoder layer's four linears at 16,384 tokens, forward + backward:
     through Fp8Linear (the FP8 block-scaled path) and through torch's BF16
     linear (the vendor BLAS), on the same shapes."""
@@ -599,7 +599,7 @@ def main():
                           if k.startswith("gemm")) / cfg_layers
         result["next_rows"] = {**bf16_comparison(torch, fp8, cfg_obj, fp8_gemm_ms),
                                **dgrad_epilogue_quantization(torch, fp8, cfg_obj),
-                               **next_rows(torch, fp8)}
+                               **fp8_linear_comparison(torch, fp8)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_fraction)
     else:
