@@ -408,6 +408,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
     }
 
     // epilogue: lane owns C[i][j .. j+3]; split s writes its own FP32 slice
+    if constexpr (OUT_BF16 && !QOUT) __syncthreads();   // every wave done with the LDS tiles
     if (j0 + 128 * wj >= J) return;
     if constexpr (QOUT) {
         const int64_t jt = j0 + 128 * wj;                  // first column of the row tiles
@@ -438,6 +439,37 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
                               bf16_lo(pk[js][1]) * ts.inv, bf16_hi(pk[js][1]) * ts.inv);
             }
             if (g == 0) Cs[i * (J / kTile) + jt / kTile] = ts.s;
+        }
+        return;
+    }
+    if constexpr (OUT_BF16) {
+        // Restage the wave's 64x128 BF16 patch through LDS (the tiles are no
+        // longer needed) so that it leaves as whole 256-byte rows in 16-byte
+        // stores; 16-byte chunks are XOR-swizzled by row.
+        uint8_t* stage = (wave < 4 ? &As[0][0] : &Bs[0][0]) + (wave & 3) * 16384;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int row = it * 16 + r16;
+#pragma unroll
+            for (int js = 0; js < 8; ++js) {
+                const int b = js * 32 + g * 8;                 // byte offset in the row
+                const int phys = (((b >> 4) ^ (row & 15)) << 4) | (b & 15);
+                *reinterpret_cast<uint2*>(stage + row * 256 + phys) =
+                    make_uint2(pack_bf16x2(acc[it][js][0], acc[it][js][1]),
+                               pack_bf16x2(acc[it][js][2], acc[it][js][3]));
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);               // lgkmcnt(0): the wave's LDS writes
+        __builtin_amdgcn_wave_barrier();
+        uint16_t* Cb = reinterpret_cast<uint16_t*>(C);
+#pragma unroll
+        for (int pass = 0; pass < 16; ++pass) {
+            const int row = pass * 4 + (lane >> 4);
+            const int c = lane & 15;                           // 16-byte chunk of the row
+            const uint4 w =
+                *reinterpret_cast<const uint4*>(stage + row * 256 + ((c ^ (row & 15)) << 4));
+            const int64_t i = i0 + wi * 64 + row;
+            if (i < I) *reinterpret_cast<uint4*>(Cb + i * J + j0 + wj * 128 + c * 8) = w;
         }
         return;
     }
