@@ -408,37 +408,81 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
     }
 
     // epilogue: lane owns C[i][j .. j+3]; split s writes its own FP32 slice
-    if constexpr (OUT_BF16 && !QOUT) __syncthreads();   // every wave done with the LDS tiles
+    if constexpr (OUT_BF16) __syncthreads();   // every wave done with the LDS tiles
     if (j0 + 128 * wj >= J) return;
     if constexpr (QOUT) {
         const int64_t jt = j0 + 128 * wj;                  // first column of the row tiles
+        uint8_t* stage = (wave < 4 ? &As[0][0] : &Bs[0][0]) + (wave & 3) * 16384;
+        // Scales of the row tiles from the BF16-rounded values.
+        float inv[4];
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-            const int64_t i = i0 + wi * 64 + it * 16 + r16;
-            uint32_t pk[8][2];
             uint32_t m = 0;
 #pragma unroll
             for (int js = 0; js < 8; ++js) {
-                pk[js][0] = pack_bf16x2(acc[it][js][0], acc[it][js][1]);
-                pk[js][1] = pack_bf16x2(acc[it][js][2], acc[it][js][3]);
-                m = absmax_pair(absmax_pair(m, pk[js][0]), pk[js][1]);
+                m = absmax_pair(m, pack_bf16x2(acc[it][js][0], acc[it][js][1]));
+                m = absmax_pair(m, pack_bf16x2(acc[it][js][2], acc[it][js][3]));
             }
             m = absmax_fold(m);
             m = max(m, (uint32_t)__shfl_xor((int)m, 16));
             m = max(m, (uint32_t)__shfl_xor((int)m, 32));
             const TileScale ts = tile_scale(m, &g_scale_tables);
-            if (i >= I) continue;
+            inv[it] = ts.inv;
+            const int64_t i = i0 + wi * 64 + it * 16 + r16;
+            if (g == 0 && i < I) Cs[i * (J / kTile) + jt / kTile] = ts.s;
+        }
+        // The BF16 copy, when asked for, then the codes: each restaged through
+        // LDS and stored as whole rows (16-byte chunks XOR-swizzled by row).
+        if (C) {
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int row = it * 16 + r16;
+#pragma unroll
+                for (int js = 0; js < 8; ++js) {
+                    const int b = js * 32 + g * 8;
+                    const int phys = (((b >> 4) ^ (row & 15)) << 4) | (b & 15);
+                    *reinterpret_cast<uint2*>(stage + row * 256 + phys) =
+                        make_uint2(pack_bf16x2(acc[it][js][0], acc[it][js][1]),
+                                   pack_bf16x2(acc[it][js][2], acc[it][js][3]));
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0): the wave's LDS writes
+            __builtin_amdgcn_wave_barrier();
+            uint16_t* Cb = reinterpret_cast<uint16_t*>(C);
+#pragma unroll
+            for (int pass = 0; pass < 16; ++pass) {
+                const int row = pass * 4 + (lane >> 4);
+                const int c = lane & 15;
+                const uint4 w =
+                    *reinterpret_cast<const uint4*>(stage + row * 256 + ((c ^ (row & 15)) << 4));
+                const int64_t i = i0 + wi * 64 + row;
+                if (i < I) *reinterpret_cast<uint4*>(Cb + i * J + jt + c * 8) = w;
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_wave_barrier();
+        }
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int row = it * 16 + r16;
 #pragma unroll
             for (int js = 0; js < 8; ++js) {
-                const int64_t j = jt + js * 16 + 4 * g;
-                if (C)
-                    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(C) + i * J + j) =
-                        make_uint2(pk[js][0], pk[js][1]);
-                *reinterpret_cast<uint32_t*>(Cq + i * J + j) =
-                    cvt4_e4m3(bf16_lo(pk[js][0]) * ts.inv, bf16_hi(pk[js][0]) * ts.inv,
-                              bf16_lo(pk[js][1]) * ts.inv, bf16_hi(pk[js][1]) * ts.inv);
+                const uint32_t p0 = pack_bf16x2(acc[it][js][0], acc[it][js][1]);
+                const uint32_t p1 = pack_bf16x2(acc[it][js][2], acc[it][js][3]);
+                *reinterpret_cast<uint32_t*>(stage + row * 128 + ((js ^ (row & 7)) << 4) + 4 * g) =
+                    cvt4_e4m3(bf16_lo(p0) * inv[it], bf16_hi(p0) * inv[it], bf16_lo(p1) * inv[it],
+                              bf16_hi(p1) * inv[it]);
             }
-            if (g == 0) Cs[i * (J / kTile) + jt / kTile] = ts.s;
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int pass = 0; pass < 8; ++pass) {
+            const int row = pass * 8 + (lane >> 3);
+            const int c = lane & 7;                            // 16-byte chunk of the 128 codes
+            const uint4 w =
+                *reinterpret_cast<const uint4*>(stage + row * 128 + ((c ^ (row & 7)) << 4));
+            const int64_t i = i0 + wi * 64 + row;
+            if (i < I) *reinterpret_cast<uint4*>(Cq + i * J + jt + c * 16) = w;
         }
         return;
     }
