@@ -266,3 +266,38 @@ def test_block_every_significand():
     q, qt, s, oq, oqt, os_ = _block_both(bits)
     _assert_codes(to_np(q), to_np(s), oq, os_, "block every significand")
     assert np.array_equal(to_np(qt), oqt)
+
+
+@pytest.mark.parametrize("which", ["rowtile", "transposed", "dual", "block"])
+def test_e4m3_grid_values_round_trip(which):
+    """Values already on the E4M3 grid, with a 448 in every tile (so every
+    scale is exactly 1), come back as their own codes on every quantizer."""
+    rng = np.random.default_rng(60)
+    t = oracle.e4m3_table()
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    M, C = 256, 384
+    codes = rng.choice(finite, size=(M, C)).astype(np.uint8)
+    codes[:, ::128] = 0x7E                                   # 448 in every row tile
+    codes[::128, :] = 0x7E                                   # and in every token-axis tile
+    vals = t[codes].astype(np.float32)
+    vals[codes == 0x80] = -0.0
+    bits = inputs.bf16_bits(vals)
+    x = to_dev_bf16(bits)
+    if which == "rowtile":
+        q, s = fp8.fp8_quantize_rowtile(x)
+        got_q, got_s, want = to_np(q), to_np(s), codes
+    elif which == "transposed":
+        qt, st = fp8.fp8_quantize_transposed(x)
+        got_q, got_s, want = to_np(qt), to_np(st), codes.T
+    elif which == "dual":
+        q, s, qt, st = fp8.fp8_quantize_dual(x)
+        assert np.array_equal(to_np(qt), codes.T) and np.all(to_np(st) == 1.0)
+        got_q, got_s, want = to_np(q), to_np(s), codes
+    else:
+        q, qt, s = fp8.fp8_quantize_block(x)
+        assert np.array_equal(to_np(qt), codes.T)
+        got_q, got_s, want = to_np(q), to_np(s), codes
+    torch.cuda.synchronize()
+    assert np.all(got_s == 1.0)
+    # -0 and +0 keep their sign; every other code is its own
+    assert np.array_equal(got_q, want)
