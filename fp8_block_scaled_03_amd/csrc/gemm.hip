@@ -20,24 +20,26 @@
 //
 // Two kernels share that arithmetic:
 //   gemm_bs_fp8_kernel      workgroup tile 128 (i) x 128 (j) x 128 (k), four
-//                           waves of 64x64, two workgroups per CU; used for
-//                           wgrad (two per-row scales per fold) and for grids
-//                           too small to give every CU a 256x256 tile; can
-//                           split the contraction (FP32 slices in a caller
-//                           workspace, summed in a fixed order).
-//   gemm_bs_fp8_big_kernel  256 x 256 x 128, eight waves of 64x128, one
-//                           workgroup per CU; fprop and dgrad.  Each wave
-//                           widens its A fragments once per block and keeps
-//                           them in registers while B fragments stream.
-// Both stage the FP8 tiles of the next block in LDS with direct global->LDS
-// loads (double buffered, 16-byte chunks XOR-swizzled by row so the fragment
-// reads are bank-conflict free) while the current block is contracted, and
-// hand out output tiles in an XCD-aware grouped order (gemm_common.h).  The
-// MFMA operands are swapped (B fragment as the first source) so that each
-// lane owns four consecutive output columns of one row and stores them as one
-// vector.
+//                           waves of 64x64, two workgroups per CU; both FP8
+//                           tiles staged in LDS by direct global->LDS loads
+//                           (double buffered, 16-byte chunks XOR-swizzled by
+//                           row) and widened by every wave that reads them.
+//                           Used for wgrad while the 256x256 tiles alone fill
+//                           the CUs, and for grids too small to give every CU
+//                           a 256x256 tile.
+//   gemm_bs_fp8_big_kernel  256 x 256 x 128, eight waves of 32x256, one
+//                           workgroup per CU; fprop, dgrad (also with the
+//                           quantizing epilogue) and the other wgrads.  B is
+//                           widened once per block into an FP16 LDS tile, A
+//                           goes straight to registers.
+// Both can split the contraction (FP32 slices in a caller workspace, summed
+// in a fixed order) and hand out output tiles in an XCD-aware grouped order
+// (gemm_common.h).  The MFMA operands are swapped (B fragment as the first
+// source) so that each lane owns four consecutive output columns of one row
+// and stores them as one vector.
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 #include "device_common.h"
 #include "gemm_common.h"
@@ -234,214 +236,266 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bs_fp8_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Large-tile kernel: workgroup tile 256 (i) x 256 (j) x 128 (k), eight waves
-// in a 4 (i) x 2 (j) grid, each wave a 64 x 128 patch.  A wave widens its 64
-// A rows to FP16 once per block and keeps them in registers (64 VGPRs), then
-// streams its eight 16-row B subtiles: per subtile it widens one 8-code chunk
-// at a time and runs the 4-instruction MFMA chain for its four A subtiles, so
-// 192 widenings feed 128 MFMAs (1.5 per MFMA, against 2 in the small kernel).
-// Tiles are ordered for the L2s: each XCD (the hardware deals workgroups to
-// the eight XCDs round-robin) gets a contiguous chunk of the tile order, and
-// the order walks groups of four tile rows column by column, so the tiles an
-// XCD runs together share A and B rows.  gridDim.y splits the contraction:
-// split s sums blocks [s*nps, (s+1)*nps) into its own FP32 slice of C.
+// Large-tile kernel: workgroup tile 256 (i) x 256 (j) x 128 (k), eight waves,
+// wave w owning the 32 x 256 output patch of rows 32w .. 32w+31.
+//   B: the 256 x 128 codes of a block are widened ONCE, cooperatively (lane l
+//      of wave w takes 64 codes of row 32w + l%32), and stored in LDS as FP16
+//      (64 KB, double buffered); every wave reads its B fragments from there.
+//   A: a wave's 32 rows are its own, so they go straight from global memory
+//      to registers and are widened once per block.
+// 64 widenings feed a wave's 128 MFMAs per block (0.5 per MFMA; 1.5 when every
+// wave widens the B fragments it reads from an FP8 tile), so the VALU work
+// (widening and the scale fold) stays well below the MFMA time.
+// Per block: the next block's B codes are requested at the top; after the
+// fourth of eight MFMA groups they are widened and stored into the other FP16
+// buffer in one burst, and the next block's A codes are requested.
+// The FP16 B tile is stored in fragment order: the 16 bytes that lane l reads
+// for MFMA chunk c of B subtile js sit at ((4 js + c) * 64 + l) * 16, so every
+// fragment read is one contiguous 1 KB block (gfx950's LDS serves those
+// without bank conflicts; a row-major tile with an XOR swizzle of its 16-byte
+// chunks still conflicts two ways).  A thread widening row R, codes
+// [8q, 8q+8), writes them where lane (R % 16) + 16 (q / 4) finds them for
+// chunk q % 4 of subtile R / 16; eight consecutive lanes always write eight
+// different rows mod 8, which keeps those stores conflict-free as well.
+// The contraction order inside a block is permuted alike for A and B: lane
+// (r16, g) supplies codes [32g + 8c, 32g + 8c + 8) of its row to MFMA chunk c,
+// so one 32-byte global load per row gives a lane its four chunks.
+// Tiles are ordered for the L2s (tile_coords); gridDim.y splits the
+// contraction: split s sums blocks [s*nps, (s+1)*nps) into its own FP32 slice
+// of C.
+// QOUT: the epilogue also quantizes the BF16 output in 1x128 row tiles (the
+// rule of quant_rowtile_kernel) and stores codes Cq [I, J] and scales
+// Cs [I, J/128]; C (BF16) may then be null.  A wave's 256 output columns of a
+// row are two such tiles, each held by the four lanes r16 + 16g.
 // ---------------------------------------------------------------------------
 constexpr int kBigM = 256;
 constexpr int kBigN = 256;
 constexpr int kBigThreads = 512;
-constexpr int kBigTile = kBigM * kBK;      // one FP8 operand tile: 32 KB
-// QOUT: the epilogue also quantizes the BF16 output in 1x128 row tiles (the
-// rule of quant_rowtile_kernel) and stores codes Cq [I, J] and scales
-// Cs [I, J/128]; C (BF16) may then be null.  A wave's 128 output columns of a
-// row are exactly one such tile, held by the four lanes r16 + 16g.
+constexpr int kF16Tile = 256 * 256;        // FP16 B tile: 256 rows x 256 bytes
+
+__device__ __forceinline__ int f16_frag_off(int row, int q) {
+    return (((row >> 4) * 4 + (q & 3)) * 64 + (q >> 2) * 16 + (row & 15)) * 16;
+}
+
 template <int MODE, bool OUT_BF16, bool QOUT = false>
 __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
     const float* __restrict__ sB, void* __restrict__ C, int64_t I, int64_t J, int64_t Kc,
     int tiles_i, int tiles_j, int nps, uint8_t* __restrict__ Cq = nullptr,
     float* __restrict__ Cs = nullptr) {
-    __shared__ __align__(16) uint8_t As[2][kBigTile];
-    __shared__ __align__(16) uint8_t Bs[2][kBigTile];
-    __shared__ __align__(16) float sAs[2][kBigM];
-    __shared__ __align__(16) float sBs[2][kBigN];
+    __shared__ __align__(16) uint8_t Bh[2][kF16Tile];
+    __shared__ __align__(16) float sBs[2][MODE == kScaleRow ? kBigN : 4];   // per-row B scales
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wi = wave & 3, wj = wave >> 2;
+    const int r16 = lane & 15;
+    const int g = lane >> 4;
     int ti, tj;
     tile_coords(blockIdx.x, tiles_i, tiles_j, &ti, &tj);
     const int64_t i0 = (int64_t)ti * kBigM, j0 = (int64_t)tj * kBigN;
     const int nkb_all = (int)(Kc / kBK);
     const int kb0 = blockIdx.y * nps;
-    const int kb1 = min(nkb_all, kb0 + nps);
-    const int nkb = kb1 - kb0;
-    const int nkb_row = nkb_all;                  // scale row stride (blocks per row)
-    const int64_t jb_count = J / kBN;             // 128-wide column blocks of B
+    const int nkb = min(nkb_all, kb0 + nps) - kb0;
+    const int64_t jb_count = J / kBN;
+    const bool j_full = j0 + kBigN <= J;             // else only the first 128 columns exist
 
-    // Direct global -> LDS loads.  Waves 0..3 fill the 32 KB A and B tiles
-    // (wave w: 1 KB pieces 8w .. 8w+7, 8 rows each; lane l lands at row
-    // 8*piece + l/8, physical chunk l%8 of the swizzle); waves 4..7, which
-    // share SIMDs with them, only load scales and go straight on to their
-    // MFMAs after each barrier.  For this lane, piece 8w + j is row
-    // prow + 8j with swizzled chunk pc (j even) or pc ^ 4 (j odd).
-    const int prow = 64 * (wave & 3) + (lane >> 3);
-    const int pc = (lane & 7) ^ ((prow >> 1) & 7);
-    // Scales: waves 0..3 load the A-row scales of rows 64w + lane, waves 4..7
-    // the B scales of rows 64(w-4) + lane (per row, or their column block's).
-    const float* s_src;
-    int64_t s_step;                               // stride per contraction block
-    if (wave < 4) {
-        s_src = sA + min(i0 + 64 * wave + lane, I - 1) * nkb_row;
-        s_step = 1;
-    } else {
-        int64_t jr = min(j0 + 64 * (wave - 4) + lane, J - 1);
-        if (MODE == kScaleRow) {
-            s_src = sB + jr * nkb_row;
-            s_step = 1;
-        } else if (MODE == kScaleBlock) {
-            s_src = sB + (jr / kBN) * nkb_row;
-            s_step = 1;
-        } else {
-            s_src = sB + jr / kBN;
-            s_step = jb_count;
-        }
-    }
-
-    auto issue_loads = [&](int kb, int buf) {
-        const int64_t koff = (int64_t)kb * kBK;
-        if (wave < 4) {
-            // Recomputed per call (the empty asm hides the loop invariance):
-            // sixteen precomputed 64-bit addresses would cost 32 registers.
-            int pr = prow, pcc = pc;
-            asm volatile("" : "+v"(pr), "+v"(pcc));
+    // A: rows 32w + 16it + r16 (clamped; rows past I are never stored), the
+    // lane's 32 bytes [32g, 32g+32) of each block.
+    const uint8_t* a_src[2];
+    const float* sa_src[2];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int row = pr + 8 * j;
-                const int c = (j & 1) ? (pcc ^ 4) : pcc;
-                __builtin_amdgcn_global_load_lds(A + min(i0 + row, I - 1) * Kc + koff + c * 16,
-                                                 (lds_void*)(&As[buf][(8 * wave + j) * 1024]), 16,
-                                                 0, 0);
-                __builtin_amdgcn_global_load_lds(B + min(j0 + row, J - 1) * Kc + koff + c * 16,
-                                                 (lds_void*)(&Bs[buf][(8 * wave + j) * 1024]), 16,
-                                                 0, 0);
-            }
+    for (int it = 0; it < 2; ++it) {
+        const int64_t row = min(i0 + 32 * wave + 16 * it + r16, I - 1);
+        a_src[it] = A + row * Kc + 32 * g;
+        sa_src[it] = sA + row * nkb_all;
+    }
+    // B: lane l of wave w widens bytes [64h, 64h+64) of row 32w + l%32
+    // (h = l/32).
+    const int brow = 32 * wave + (lane & 31);
+    const int bh = lane >> 5;
+    const int64_t bj = min(j0 + brow, J - 1);
+    const uint8_t* b_src = B + bj * Kc + 64 * bh;
+    const float* sbr_src = MODE == kScaleRow ? sB + bj * nkb_all : sB;   // scale row of B row brow
+    const int64_t jb0 = j0 / kBN;
+    const int64_t jb1 = min(jb0 + 1, jb_count - 1);
+
+    uint4 an[2][2];           // next block's A codes
+    uint4 bn[4];              // next block's B codes
+    float san[2], sbn0 = 0.f, sbn1 = 0.f, sbrn = 0.f;
+    auto load_a = [&](int kb) {
+        const int64_t koff = (int64_t)kb * kBK;
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            an[it][0] = *reinterpret_cast<const uint4*>(a_src[it] + koff);
+            an[it][1] = *reinterpret_cast<const uint4*>(a_src[it] + koff + 16);
+            san[it] = sa_src[it][kb];
         }
-        float* sdst = (wave < 4) ? &sAs[buf][64 * wave] : &sBs[buf][64 * (wave - 4)];
-        __builtin_amdgcn_global_load_lds(s_src + kb * s_step, (lds_void*)sdst, 4, 0, 0);
+        if (MODE == kScaleBlock) {
+            sbn0 = sB[jb0 * nkb_all + kb];
+            sbn1 = sB[jb1 * nkb_all + kb];
+        } else if (MODE == kScaleBlockT) {
+            sbn0 = sB[(int64_t)kb * jb_count + jb0];
+            sbn1 = sB[(int64_t)kb * jb_count + jb1];
+        }
+    };
+    auto load_b = [&](int kb) {
+        const int64_t koff = (int64_t)kb * kBK;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bn[q] = *reinterpret_cast<const uint4*>(b_src + koff + 16 * q);
+        if (MODE == kScaleRow) sbrn = sbr_src[kb];
+    };
+    // Widen and store codes [16p, 16p+16) of the lane's 64 (two chunks).
+    // The opaque register dependence (an asm statement stays between the
+    // LDS reads around it) keeps the compiler from hoisting the widening,
+    // and with it the wait for these loads, towards the top of the block,
+    // where the codes are still in flight.
+    auto store_b = [&](int buf, int p) {
+        uint8_t* dst = Bh[buf];
+        // Row-scaled B (wgrad, two VALU operations per output element in the
+        // fold) runs faster with the widening fenced off from the MFMA groups
+        // around it; the block-scaled modes run faster without the fence.
+        if constexpr (MODE == kScaleRow) __builtin_amdgcn_sched_barrier(0);
+        uint4 w = bn[p];
+        asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+        *reinterpret_cast<v8h*>(dst + f16_frag_off(brow, 8 * bh + 2 * p)) = widen8(w.x, w.y);
+        *reinterpret_cast<v8h*>(dst + f16_frag_off(brow, 8 * bh + 2 * p + 1)) = widen8(w.z, w.w);
+        if (MODE == kScaleRow && p == 0) sBs[buf][brow] = sbrn;   // both halves of the row write it
     };
 
-    v4f acc[4][8];
+    // B subtiles per MFMA group: two (four independent chains) where the fold
+    // is one FMA per element, one where it also needs a scale product.
+    constexpr int JJ = 2;
+    v4f acc[2][16];
 #pragma unroll
-    for (int it = 0; it < 4; ++it)
+    for (int it = 0; it < 2; ++it)
 #pragma unroll
-        for (int js = 0; js < 8; ++js) acc[it][js] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int js = 0; js < 16; ++js) acc[it][js] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    const int r16 = lane & 15;
-    const int g = lane >> 4;
-
-    if (nkb > 0) issue_loads(kb0, 0);
-    for (int k = 0; k < nkb; ++k) {
+    if (nkb > 0) {
+        load_b(kb0);
+        load_a(kb0);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) store_b(0, p);
+    }
+    // One block; MORE: the next block is loaded and staged during this one.
+    // The last block runs as its own copy, so the loop body has no branch.
+    auto run_block = [&](int k, auto more_tag) __attribute__((always_inline)) {
+        constexpr bool more = decltype(more_tag)::value;
         const int buf = k & 1;
-        wait_global_loads();
-        __syncthreads();
-        if (k + 1 < nkb) issue_loads(kb0 + k + 1, buf ^ 1);
-
-        const uint8_t* At = As[buf];
-        const uint8_t* Bt = Bs[buf];
-        // This wave's A rows for the whole block, widened once: af[it][c] is
-        // MFMA chunk c (bytes [8c, 8c+8) of the lane's 32) of subtile it.
-        v8h af[4][4];
+        __syncthreads();          // B of this block is in Bh[buf]; all waves are done with Bh[buf^1]
+        v8h af[2][4];
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int row = wi * 64 + it * 16 + r16;
-            uint4 lo = *reinterpret_cast<const uint4*>(At + lds_off(row, 2 * g));
-            uint4 hi = *reinterpret_cast<const uint4*>(At + lds_off(row, 2 * g + 1));
-            af[it][0] = widen8(lo.x, lo.y);
-            af[it][1] = widen8(lo.z, lo.w);
-            af[it][2] = widen8(hi.x, hi.y);
-            af[it][3] = widen8(hi.z, hi.w);
+        for (int it = 0; it < 2; ++it) {
+            af[it][0] = widen8(an[it][0].x, an[it][0].y);
+            af[it][1] = widen8(an[it][0].z, an[it][0].w);
+            af[it][2] = widen8(an[it][1].x, an[it][1].y);
+            af[it][3] = widen8(an[it][1].z, an[it][1].w);
         }
-        float sa[4];
+        float cs0[2], cs1[2];
 #pragma unroll
-        for (int it = 0; it < 4; ++it) sa[it] = sAs[buf][wi * 64 + it * 16 + r16];
-        if (MODE != kScaleRow) {
-            const float sb = sBs[buf][128 * wj];      // the wave's 128 columns share one block scale
-#pragma unroll
-            for (int it = 0; it < 4; ++it) sa[it] = sa[it] * sb;
+        for (int it = 0; it < 2; ++it) {
+            cs0[it] = san[it] * sbn0;         // kScaleRow: unused
+            cs1[it] = san[it] * sbn1;
         }
+        float sa[2] = {san[0], san[1]};
+        if constexpr (more) load_b(kb0 + k + 1);      // widened in the middle of this block
+        const uint8_t* Bt = Bh[buf];
 #pragma unroll
-        for (int js = 0; js < 8; ++js) {
-            const int row = wj * 128 + js * 16 + r16;
-            uint4 lo = *reinterpret_cast<const uint4*>(Bt + lds_off(row, 2 * g));
-            uint4 hi = *reinterpret_cast<const uint4*>(Bt + lds_off(row, 2 * g + 1));
-            v4f p[4];
+        for (int jp = 0; jp < 16 / JJ; ++jp) {
+            v4f p[JJ][2];
 #pragma unroll
-            for (int it = 0; it < 4; ++it) p[it] = v4f{0.f, 0.f, 0.f, 0.f};
+            for (int jj = 0; jj < JJ; ++jj)
+#pragma unroll
+                for (int it = 0; it < 2; ++it) p[jj][it] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const uint32_t w0 = c == 0 ? lo.x : c == 1 ? lo.z : c == 2 ? hi.x : hi.z;
-                const uint32_t w1 = c == 0 ? lo.y : c == 1 ? lo.w : c == 2 ? hi.y : hi.w;
-                const v8h bf = widen8(w0, w1);
+                v8h bf[JJ];
 #pragma unroll
-                for (int it = 0; it < 4; ++it)
-                    p[it] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf, af[it][c], p[it], 0, 0, 0);
+                for (int jj = 0; jj < JJ; ++jj)
+                    bf[jj] = *reinterpret_cast<const v8h*>(
+                        Bt + ((4 * (JJ * jp + jj) + c) * 64 + lane) * 16);
+#pragma unroll
+                for (int jj = 0; jj < JJ; ++jj)
+#pragma unroll
+                    for (int it = 0; it < 2; ++it)
+                        // D[j][i]: j = 4g+v (rows of the B subtile), i = r16 (rows of the A subtile)
+                        p[jj][it] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[jj], af[it][c],
+                                                                            p[jj][it], 0, 0, 0);
             }
-            if (MODE != kScaleRow) {
 #pragma unroll
-                for (int it = 0; it < 4; ++it)
+            for (int jj = 0; jj < JJ; ++jj) {
+                const int js = JJ * jp + jj;
+                if (MODE != kScaleRow) {
 #pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        acc[it][js][v] = __builtin_fmaf(p[it][v], sa[it], acc[it][js][v]);
-            } else {
-                const float4 sb =
-                    *reinterpret_cast<const float4*>(&sBs[buf][wj * 128 + js * 16 + 4 * g]);
+                    for (int it = 0; it < 2; ++it) {
+                        const float cs = js < 8 ? cs0[it] : cs1[it];
 #pragma unroll
-                for (int it = 0; it < 4; ++it) {
-                    acc[it][js][0] = __builtin_fmaf(p[it][0], sa[it] * sb.x, acc[it][js][0]);
-                    acc[it][js][1] = __builtin_fmaf(p[it][1], sa[it] * sb.y, acc[it][js][1]);
-                    acc[it][js][2] = __builtin_fmaf(p[it][2], sa[it] * sb.z, acc[it][js][2]);
-                    acc[it][js][3] = __builtin_fmaf(p[it][3], sa[it] * sb.w, acc[it][js][3]);
+                        for (int v = 0; v < 4; ++v)
+                            acc[it][js][v] = __builtin_fmaf(p[jj][it][v], cs, acc[it][js][v]);
+                    }
+                } else {
+                    // (P * sB(j)) * sA(i): the column scale is applied in place,
+                    // so the fold needs no registers for scale products.
+                    const float4 sb = *reinterpret_cast<const float4*>(&sBs[buf][16 * js + 4 * g]);
+#pragma unroll
+                    for (int it = 0; it < 2; ++it) {
+                        acc[it][js][0] = __builtin_fmaf(p[jj][it][0] * sb.x, sa[it], acc[it][js][0]);
+                        acc[it][js][1] = __builtin_fmaf(p[jj][it][1] * sb.y, sa[it], acc[it][js][1]);
+                        acc[it][js][2] = __builtin_fmaf(p[jj][it][2] * sb.z, sa[it], acc[it][js][2]);
+                        acc[it][js][3] = __builtin_fmaf(p[jj][it][3] * sb.w, sa[it], acc[it][js][3]);
+                    }
+                }
+            }
+            if constexpr (more) {
+                if (jp == 3) {
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) store_b(buf ^ 1, p);   // B of the next block, widened once
+                    load_a(kb0 + k + 1);      // its A codes, in flight until the next block
                 }
             }
         }
-    }
+    };
+    for (int k = 0; k + 1 < nkb; ++k) run_block(k, std::true_type{});
+    if (nkb > 0) run_block(nkb - 1, std::false_type{});
 
     // epilogue: lane owns C[i][j .. j+3]; split s writes its own FP32 slice
     if constexpr (OUT_BF16) __syncthreads();   // every wave done with the LDS tiles
-    if (j0 + 128 * wj >= J) return;
+    const int js_end = j_full ? 16 : 8;
     if constexpr (QOUT) {
-        const int64_t jt = j0 + 128 * wj;                  // first column of the row tiles
-        uint8_t* stage = (wave < 4 ? &As[0][0] : &Bs[0][0]) + (wave & 3) * 16384;
-        // Scales of the row tiles from the BF16-rounded values.
-        float inv[4];
+        uint8_t* stage = &Bh[0][0] + wave * 16384;
+        // Scales of the row tiles (two per row: columns j0 .. j0+127 and
+        // j0+128 .. j0+255) from the BF16-rounded values.
+        float inv[2][2];
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            uint32_t m = 0;
+        for (int it = 0; it < 2; ++it) {
+            const int64_t i = i0 + 32 * wave + 16 * it + r16;
 #pragma unroll
-            for (int js = 0; js < 8; ++js) {
-                m = absmax_pair(m, pack_bf16x2(acc[it][js][0], acc[it][js][1]));
-                m = absmax_pair(m, pack_bf16x2(acc[it][js][2], acc[it][js][3]));
+            for (int t = 0; t < 2; ++t) {
+                uint32_t m = 0;
+#pragma unroll
+                for (int js = 8 * t; js < 8 * t + 8; ++js) {
+                    m = absmax_pair(m, pack_bf16x2(acc[it][js][0], acc[it][js][1]));
+                    m = absmax_pair(m, pack_bf16x2(acc[it][js][2], acc[it][js][3]));
+                }
+                m = absmax_fold(m);
+                m = max(m, (uint32_t)__shfl_xor((int)m, 16));
+                m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+                const TileScale ts = tile_scale(m, &g_scale_tables);
+                inv[it][t] = ts.inv;
+                if (g == 0 && i < I && (t == 0 || j_full))
+                    Cs[i * jb_count + jb0 + t] = ts.s;
             }
-            m = absmax_fold(m);
-            m = max(m, (uint32_t)__shfl_xor((int)m, 16));
-            m = max(m, (uint32_t)__shfl_xor((int)m, 32));
-            const TileScale ts = tile_scale(m, &g_scale_tables);
-            inv[it] = ts.inv;
-            const int64_t i = i0 + wi * 64 + it * 16 + r16;
-            if (g == 0 && i < I) Cs[i * (J / kTile) + jt / kTile] = ts.s;
         }
-        // The BF16 copy, when asked for, then the codes: each restaged through
-        // LDS and stored as whole rows (16-byte chunks XOR-swizzled by row).
         if (C) {
 #pragma unroll
-            for (int it = 0; it < 4; ++it) {
-                const int row = it * 16 + r16;
+            for (int it = 0; it < 2; ++it) {
+                const int row = 16 * it + r16;
 #pragma unroll
-                for (int js = 0; js < 8; ++js) {
+                for (int js = 0; js < 16; ++js) {
                     const int b = js * 32 + g * 8;
                     const int phys = (((b >> 4) ^ (row & 15)) << 4) | (b & 15);
-                    *reinterpret_cast<uint2*>(stage + row * 256 + phys) =
+                    *reinterpret_cast<uint2*>(stage + row * 512 + phys) =
                         make_uint2(pack_bf16x2(acc[it][js][0], acc[it][js][1]),
                                    pack_bf16x2(acc[it][js][2], acc[it][js][3]));
                 }
@@ -451,54 +505,54 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
             uint16_t* Cb = reinterpret_cast<uint16_t*>(C);
 #pragma unroll
             for (int pass = 0; pass < 16; ++pass) {
-                const int row = pass * 4 + (lane >> 4);
-                const int c = lane & 15;
+                const int row = 2 * pass + (lane >> 5);
+                const int c = lane & 31;
                 const uint4 w =
-                    *reinterpret_cast<const uint4*>(stage + row * 256 + ((c ^ (row & 15)) << 4));
-                const int64_t i = i0 + wi * 64 + row;
-                if (i < I) *reinterpret_cast<uint4*>(Cb + i * J + jt + c * 8) = w;
+                    *reinterpret_cast<const uint4*>(stage + row * 512 + ((c ^ (row & 15)) << 4));
+                const int64_t i = i0 + 32 * wave + row;
+                if (i < I && (c < 16 || j_full))
+                    *reinterpret_cast<uint4*>(Cb + i * J + j0 + c * 8) = w;
             }
             __builtin_amdgcn_s_waitcnt(0xC07F);
             __builtin_amdgcn_wave_barrier();
         }
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int row = it * 16 + r16;
+        for (int it = 0; it < 2; ++it) {
+            const int row = 16 * it + r16;
 #pragma unroll
-            for (int js = 0; js < 8; ++js) {
+            for (int js = 0; js < 16; ++js) {
+                const float iv = inv[it][js >> 3];
                 const uint32_t p0 = pack_bf16x2(acc[it][js][0], acc[it][js][1]);
                 const uint32_t p1 = pack_bf16x2(acc[it][js][2], acc[it][js][3]);
-                *reinterpret_cast<uint32_t*>(stage + row * 128 + ((js ^ (row & 7)) << 4) + 4 * g) =
-                    cvt4_e4m3(bf16_lo(p0) * inv[it], bf16_hi(p0) * inv[it], bf16_lo(p1) * inv[it],
-                              bf16_hi(p1) * inv[it]);
+                *reinterpret_cast<uint32_t*>(stage + row * 256 + ((js ^ (row & 15)) << 4) + 4 * g) =
+                    cvt4_e4m3(bf16_lo(p0) * iv, bf16_hi(p0) * iv, bf16_lo(p1) * iv, bf16_hi(p1) * iv);
             }
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int pass = 0; pass < 8; ++pass) {
-            const int row = pass * 8 + (lane >> 3);
-            const int c = lane & 7;                            // 16-byte chunk of the 128 codes
+            const int row = 4 * pass + (lane >> 4);
+            const int c = lane & 15;                           // 16-byte chunk of the 256 codes
             const uint4 w =
-                *reinterpret_cast<const uint4*>(stage + row * 128 + ((c ^ (row & 7)) << 4));
-            const int64_t i = i0 + wi * 64 + row;
-            if (i < I) *reinterpret_cast<uint4*>(Cq + i * J + jt + c * 16) = w;
+                *reinterpret_cast<const uint4*>(stage + row * 256 + ((c ^ (row & 15)) << 4));
+            const int64_t i = i0 + 32 * wave + row;
+            if (i < I && (c < 8 || j_full)) *reinterpret_cast<uint4*>(Cq + i * J + j0 + c * 16) = w;
         }
         return;
     }
     if constexpr (OUT_BF16) {
-        // Restage the wave's 64x128 BF16 patch through LDS (the tiles are no
-        // longer needed) so that it leaves as whole 256-byte rows in 16-byte
-        // stores; 16-byte chunks are XOR-swizzled by row.
-        uint8_t* stage = (wave < 4 ? &As[0][0] : &Bs[0][0]) + (wave & 3) * 16384;
+        // Restage the wave's 32x256 BF16 patch through LDS so that it leaves
+        // as whole 512-byte rows in 16-byte stores.
+        uint8_t* stage = &Bh[0][0] + wave * 16384;
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int row = it * 16 + r16;
+        for (int it = 0; it < 2; ++it) {
+            const int row = 16 * it + r16;
 #pragma unroll
-            for (int js = 0; js < 8; ++js) {
+            for (int js = 0; js < 16; ++js) {
                 const int b = js * 32 + g * 8;                 // byte offset in the row
                 const int phys = (((b >> 4) ^ (row & 15)) << 4) | (b & 15);
-                *reinterpret_cast<uint2*>(stage + row * 256 + phys) =
+                *reinterpret_cast<uint2*>(stage + row * 512 + phys) =
                     make_uint2(pack_bf16x2(acc[it][js][0], acc[it][js][1]),
                                pack_bf16x2(acc[it][js][2], acc[it][js][3]));
             }
@@ -508,33 +562,26 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
         uint16_t* Cb = reinterpret_cast<uint16_t*>(C);
 #pragma unroll
         for (int pass = 0; pass < 16; ++pass) {
-            const int row = pass * 4 + (lane >> 4);
-            const int c = lane & 15;                           // 16-byte chunk of the row
+            const int row = 2 * pass + (lane >> 5);
+            const int c = lane & 31;                           // 16-byte chunk of the row
             const uint4 w =
-                *reinterpret_cast<const uint4*>(stage + row * 256 + ((c ^ (row & 15)) << 4));
-            const int64_t i = i0 + wi * 64 + row;
-            if (i < I) *reinterpret_cast<uint4*>(Cb + i * J + j0 + wj * 128 + c * 8) = w;
+                *reinterpret_cast<const uint4*>(stage + row * 512 + ((c ^ (row & 15)) << 4));
+            const int64_t i = i0 + 32 * wave + row;
+            if (i < I && (c < 16 || j_full)) *reinterpret_cast<uint4*>(Cb + i * J + j0 + c * 8) = w;
         }
         return;
     }
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int64_t i = i0 + wi * 64 + it * 16 + r16;
+    for (int it = 0; it < 2; ++it) {
+        const int64_t i = i0 + 32 * wave + 16 * it + r16;
         if (i >= I) continue;
+        float* Cf = reinterpret_cast<float*>(C) + (int64_t)blockIdx.y * I * J;
 #pragma unroll
-        for (int js = 0; js < 8; ++js) {
-            const int64_t j = j0 + wj * 128 + js * 16 + 4 * g;
-            if (OUT_BF16) {
-                uint16_t* Cb = reinterpret_cast<uint16_t*>(C);
-                uint2 pk;
-                pk.x = pack_bf16x2(acc[it][js][0], acc[it][js][1]);
-                pk.y = pack_bf16x2(acc[it][js][2], acc[it][js][3]);
-                *reinterpret_cast<uint2*>(Cb + i * J + j) = pk;
-            } else {
-                float* Cf = reinterpret_cast<float*>(C) + (int64_t)blockIdx.y * I * J;
+        for (int js = 0; js < 16; ++js) {
+            const int64_t j = j0 + 16 * js + 4 * g;
+            if (js < js_end)
                 *reinterpret_cast<float4*>(Cf + i * J + j) =
                     make_float4(acc[it][js][0], acc[it][js][1], acc[it][js][2], acc[it][js][3]);
-            }
         }
     }
 }

@@ -7,13 +7,12 @@
 //     C[i][j] = sum_k A[i][k] * B[j][k],   A [I, K], B [J, K] BF16,
 // contraction contiguous ("TN"), products accumulated in FP32 by the MFMA.
 //
-// Same structure as the FP8 kernels' 256x256 tile, minus the FP8-specific
-// work: workgroup tile 256 (i) x 256 (j) x 64 (k); eight waves in a 4x2 grid,
-// each a 64x128 patch of 4x8 MFMA tiles; BF16 tiles (256 rows of 128 bytes,
-// 32 KB per operand) double-buffered in LDS through direct global->LDS loads;
+// Workgroup tile 256 (i) x 256 (j) x 64 (k); eight waves in a 4x2 grid, each
+// a 64x128 patch of 4x8 MFMA tiles; BF16 tiles (256 rows of 128 bytes, 32 KB
+// per operand) double-buffered in LDS through direct global->LDS loads;
 // v_mfma_f32_16x16x32_bf16 accumulates straight into the FP32 accumulators
-// (no widening, no per-block scale fold).  This wave's A fragments for the
-// 64-wide step are read once and kept in registers; B fragments stream.
+// (nothing to widen, no per-block scale fold).  This wave's A fragments for
+// the 64-wide step are read once and kept in registers; B fragments stream.
 #include "device_common.h"
 #include "gemm_common.h"
 #include "internal.h"
