@@ -169,15 +169,17 @@ hipError_t launch_quant_block(const uint16_t* w, int64_t N, int64_t K, uint8_t* 
 // so with ROWS the workgroup reads the BF16 tile once and writes both code
 // sets and both scale sets (fp8_quantize_dual); without, only the token-axis
 // ones (fp8_quantize_transposed).
-//   Rows: thread t holds chunk t%16 (8 channels) of rows 16q + t/16, q = 0..7;
+//   512 threads: the 38 KB LDS tile allows four workgroups per CU, and with
+//   eight waves each that is eight waves per SIMD to cover the loads' latency.
+//   Rows: thread t holds chunk t%16 (8 channels) of rows 32q + t/16, q = 0..3;
 //     the 16 lanes of a row reduce its amax with four lane swaps.
 //   Columns: the tile is copied to LDS with token r stored at physical row
 //     8*(r%16) + r/16 and a 72-dword row stride, so that both the 16-byte row
 //     writes and the column reads below touch 64 distinct banks; thread
 //     (pair p, group g) then reads channels 2p, 2p+1 of tokens 16g .. 16g+15
-//     (two pairs per thread) and reduces each channel over the 8 groups.
+//     and reduces each channel over the 8 groups.
 // ---------------------------------------------------------------------------
-constexpr int kDualThreads = 256;
+constexpr int kDualThreads = 512;
 constexpr int kDualStrideDw = 72;                    // dwords per LDS token row
 
 __device__ __forceinline__ int dual_row(int r) { return ((r & 15) << 3) + (r >> 4); }
@@ -194,15 +196,15 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
     const int64_t mb = blockIdx.x / cblocks, cb = blockIdx.x % cblocks;
     const int64_t m0 = mb * kTile, c0 = cb * kTile;
     const int chunk = tid & 15;                         // 8 channels: 8*chunk .. +7
-    const int rsub = tid >> 4;                          // rows rsub + 16q
+    const int rsub = tid >> 4;                          // rows rsub + 32q
 
-    uint4 v[8];
+    uint4 v[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        v[i] = load_stream16(x + (m0 + 16 * i + rsub) * C + c0 + chunk * 8);
+    for (int i = 0; i < 4; ++i)
+        v[i] = load_stream16(x + (m0 + 32 * i + rsub) * C + c0 + chunk * 8);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = 16 * i + rsub;
+    for (int i = 0; i < 4; ++i) {
+        const int r = 32 * i + rsub;
         *reinterpret_cast<uint4*>(tile + dual_row(r) * kDualStrideDw + chunk * 4) = v[i];
     }
 
@@ -210,14 +212,14 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
 
     // Row tiles.
 #pragma unroll
-    for (int i = 0; i < 8 && ROWS; ++i) {
+    for (int i = 0; i < 4 && ROWS; ++i) {
         uint32_t m = absmax_fold(absmax_u4(0u, v[i]));
         m = max(m, (uint32_t)__shfl_xor((int)m, 1));
         m = max(m, (uint32_t)__shfl_xor((int)m, 2));
         m = max(m, (uint32_t)__shfl_xor((int)m, 4));
         m = max(m, (uint32_t)__shfl_xor((int)m, 8));
         const TileScale ts = tile_scale(m, &tab);
-        const int64_t row = m0 + 16 * i + rsub;
+        const int64_t row = m0 + 32 * i + rsub;
         *reinterpret_cast<uint2*>(q + row * C + c0 + chunk * 8) = quant8(v[i], ts.inv);
         if (chunk == 0) s[row * cblocks + cb] = ts.s;
     }
@@ -226,9 +228,8 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
     // Token-axis tiles.
     const int g = tid & 7;
     const int64_t mbn = M / kTile;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        const int p = (tid >> 3) + 32 * half;           // channel pair: 2p, 2p+1
+    {
+        const int p = tid >> 3;                         // channel pair: 2p, 2p+1
         uint32_t d[16];
         uint32_t m = 0;
 #pragma unroll
