@@ -401,6 +401,21 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
         float sa[2] = {san[0], san[1]};
         if constexpr (more) load_b(kb0 + k + 1);      // widened in the middle of this block
         const uint8_t* Bt = Bh[buf];
+        // MFMA step t = 4 jp + c reads B fragments (subtiles JJ jp + jj, chunk
+        // c).  Block-scaled modes read them kAhead steps ahead, so the MFMAs in
+        // between cover the LDS latency; the row-scaled mode has no registers
+        // to spare for more sets.
+        constexpr int kAhead = MODE != kScaleRow ? 1 : 0;
+        constexpr int kSets = kAhead + 1;
+        auto frag = [&](int t, int jj) {
+            return *reinterpret_cast<const v8h*>(
+                Bt + ((4 * (JJ * (t >> 2) + jj) + (t & 3)) * 64 + lane) * 16);
+        };
+        v8h bq[kSets][JJ];
+#pragma unroll
+        for (int t = 0; t < kAhead; ++t)
+#pragma unroll
+            for (int jj = 0; jj < JJ; ++jj) bq[t][jj] = frag(t, jj);
 #pragma unroll
         for (int jp = 0; jp < 16 / JJ; ++jp) {
             v4f p[JJ][2];
@@ -410,17 +425,17 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
                 for (int it = 0; it < 2; ++it) p[jj][it] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                v8h bf[JJ];
+                const int t = 4 * jp + c;
+                if (t + kAhead < 64 / JJ) {
 #pragma unroll
-                for (int jj = 0; jj < JJ; ++jj)
-                    bf[jj] = *reinterpret_cast<const v8h*>(
-                        Bt + ((4 * (JJ * jp + jj) + c) * 64 + lane) * 16);
+                    for (int jj = 0; jj < JJ; ++jj) bq[(t + kAhead) % kSets][jj] = frag(t + kAhead, jj);
+                }
 #pragma unroll
                 for (int jj = 0; jj < JJ; ++jj)
 #pragma unroll
                     for (int it = 0; it < 2; ++it)
                         // D[j][i]: j = 4g+v (rows of the B subtile), i = r16 (rows of the A subtile)
-                        p[jj][it] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[jj], af[it][c],
+                        p[jj][it] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bq[t % kSets][jj], af[it][c],
                                                                             p[jj][it], 0, 0, 0);
             }
 #pragma unroll
