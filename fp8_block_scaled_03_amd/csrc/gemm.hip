@@ -24,12 +24,12 @@
 //                           tiles staged in LDS by direct global->LDS loads
 //                           (double buffered, 16-byte chunks XOR-swizzled by
 //                           row) and widened by every wave that reads them.
-//                           Used for wgrad while the 256x256 tiles alone fill
-//                           the CUs, and for grids too small to give every CU
-//                           a 256x256 tile.
+//                           Used for wgrad without a split workspace when the
+//                           256x256 tiles alone fill the CUs, and for grids
+//                           too small to give every CU a 256x256 tile.
 //   gemm_bs_fp8_big_kernel  256 x 256 x 128, eight waves of 32x256, one
 //                           workgroup per CU; fprop, dgrad (also with the
-//                           quantizing epilogue) and the other wgrads.  B is
+//                           quantizing epilogue) and wgrad.  B is
 //                           widened once per block into an FP16 LDS tile, A
 //                           goes straight to registers.
 // Both can split the contraction (FP32 slices in a caller workspace, summed
@@ -402,10 +402,9 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
         if constexpr (more) load_b(kb0 + k + 1);      // widened in the middle of this block
         const uint8_t* Bt = Bh[buf];
         // MFMA step t = 4 jp + c reads B fragments (subtiles JJ jp + jj, chunk
-        // c).  Block-scaled modes read them kAhead steps ahead, so the MFMAs in
-        // between cover the LDS latency; the row-scaled mode has no registers
-        // to spare for more sets.
-        constexpr int kAhead = MODE != kScaleRow ? 1 : 0;
+        // c), kAhead steps ahead, so the MFMAs in between cover the LDS
+        // latency (two steps ahead costs more in registers than it gains).
+        constexpr int kAhead = 1;
         constexpr int kSets = kAhead + 1;
         auto frag = [&](int t, int jj) {
             return *reinterpret_cast<const v8h*>(
@@ -673,12 +672,13 @@ static Plan plan_gemm(ScaleMode mode, int64_t I, int64_t J, int64_t Kc, int num_
     const int64_t big_tiles = ((I + kBigM - 1) / kBigM) * ((J + kBigN - 1) / kBigN);
     const int64_t small_tiles = ((I + kBM - 1) / kBM) * (J / kBN);
     // fprop/dgrad: the 256x256 tile once it gives every CU a tile.  wgrad: the
-    // 256x256 tile (with a split of the contraction) while its tiles alone
-    // cannot fill the CUs; past that, the 128x128 tile, which needs no split
-    // and so moves no FP32 partials through HBM (measured in the full step).
+    // 256x256 tile whenever the contraction may be split (a caller workspace)
+    // or its tiles alone cannot fill the CUs; otherwise the 128x128 tile,
+    // whose two workgroups per CU balance the grid without a split.
     if (force == 2) p.big = true;
     else if (force == 1) p.big = false;
-    else p.big = I >= kBigM && (mode == kScaleRow ? big_tiles < cus : big_tiles >= cus);
+    else p.big = I >= kBigM && (mode == kScaleRow ? (allow_split || big_tiles < cus)
+                                                   : big_tiles >= cus);
     // Split the contraction (FP32 output only, with a caller workspace) into
     // s = 1, 2, 4, ... parts, taking the s that minimizes (full waves of
     // resident workgroups) x (contraction blocks per workgroup); ties go to
