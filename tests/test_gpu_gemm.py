@@ -114,7 +114,8 @@ def test_dgrad_parity(M, N, K, out, kernel):
         check_bf16(dx, ref, a, b, "dgrad bf16")
 
 
-WGRAD_CASES = [(256, 256, 384), (1024, 384, 256), (128, 128, 128), (2048, 512, 640)]
+WGRAD_CASES = [(256, 256, 384), (1024, 384, 256), (128, 128, 128), (2048, 512, 640),
+               (1664, 384, 640)]   # 13 contraction blocks: splits of unequal length
 
 
 @pytest.mark.parametrize("M,N,K", WGRAD_CASES)
@@ -191,6 +192,21 @@ def test_every_code_passes_exactly(kernel):
     want = t[A[:, kj]].astype(np.float32)
     got = to_np(y)
     assert np.array_equal(got, want), np.argwhere(got != want)[:5]
+
+
+@pytest.mark.parametrize("M,N", [(64, 128), (512, 640)])
+def test_zero_contraction_writes_zeros(M, N, kernel):
+    """K == 0: the sum over no blocks is zero, with either tile kernel and
+    either output type (the 256x256 kernel then issues no loads at all)."""
+    xq = torch.empty((M, 0), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((M, 0), dtype=torch.float32, device="cuda")
+    wq0 = torch.empty((N, 0), dtype=torch.uint8, device="cuda")
+    ws0 = torch.empty((N // 128, 0), dtype=torch.float32, device="cuda")
+    for dt in (torch.float32, torch.bfloat16):
+        y = torch.full((M, N), 7.0, device="cuda", dtype=dt)
+        fp8.fp8_gemm_fprop(xq, xs, wq0, ws0, out_dtype=dt, y=y)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(y).item() == 0, dt
 
 
 def test_gemm_empty_and_zero_contraction():
