@@ -298,7 +298,6 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
     const int kb0 = blockIdx.y * nps;
     const int nkb = min(nkb_all, kb0 + nps) - kb0;
     const int64_t jb_count = J / kBN;
-    const bool j_full = j0 + kBigN <= J;             // else only the first 128 columns exist
 
     // A: rows 32w + 16it + r16 (clamped; rows past I are never stored), the
     // lane's 32 bytes [32g, 32g+32) of each block.
@@ -378,6 +377,119 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
 #pragma unroll
         for (int p = 0; p < 4; ++p) store_b(0, p);
     }
+    // Output half h (columns j0 + 128h .. +127, i.e. B subtiles 8h .. 8h+7)
+    // of the tile: lane owns C[i][j .. j+3]; split s writes its own FP32
+    // slice.  Half 0 is final after the fourth MFMA group of the last block;
+    // in the block-scaled modes it leaves then, while the second half is
+    // computed.  BF16 outputs (and the
+    // codes of the quantizing epilogue) are restaged through this wave's 8 KB
+    // of Bh[lbuf ^ 1], which nothing reads or writes during the last block
+    // (lbuf: the buffer the last block reads), so that they leave as whole
+    // rows in 16-byte stores.
+    const bool j_full = j0 + kBigN <= J;             // else only the first 128 columns exist
+    // The row-scaled (FP32) instantiation has no registers for the early half.
+    constexpr bool kEarlyHalf = MODE != kScaleRow;
+    auto out_half = [&](auto h_tag, int lbuf) __attribute__((always_inline)) {
+        constexpr int h = decltype(h_tag)::value;
+        if (h == 1 && !j_full) return;
+        const int64_t jh = j0 + 128 * h;             // first column of the half
+        uint8_t* stage = &Bh[lbuf ^ 1][0] + wave * 8192;
+        // BF16 half rows (256 bytes, 16-byte chunks XOR-swizzled by row).
+        auto store_bf16 = [&](uint16_t* Cb) __attribute__((always_inline)) {
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+                const int row = 16 * it + r16;
+#pragma unroll
+                for (int jq = 0; jq < 8; ++jq) {
+                    const int js = 8 * h + jq;
+                    const int b = jq * 32 + g * 8;         // byte offset in the half row
+                    const int phys = (((b >> 4) ^ (row & 15)) << 4) | (b & 15);
+                    *reinterpret_cast<uint2*>(stage + row * 256 + phys) =
+                        make_uint2(pack_bf16x2(acc[it][js][0], acc[it][js][1]),
+                                   pack_bf16x2(acc[it][js][2], acc[it][js][3]));
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0): the wave's LDS writes
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int pass = 0; pass < 8; ++pass) {
+                const int row = 4 * pass + (lane >> 4);
+                const int c = lane & 15;                   // 16-byte chunk of the half row
+                const uint4 w =
+                    *reinterpret_cast<const uint4*>(stage + row * 256 + ((c ^ (row & 15)) << 4));
+                const int64_t i = i0 + 32 * wave + row;
+                if (i < I) *reinterpret_cast<uint4*>(Cb + i * J + jh + c * 8) = w;
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_wave_barrier();
+        };
+        if constexpr (QOUT) {
+            // Scale of the row tile (columns jh .. jh+127) from the
+            // BF16-rounded values, then the BF16 copy if asked for, then the
+            // codes (32 rows x 128 bytes, chunks XOR-swizzled by row).
+            float inv[2];
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+                uint32_t m = 0;
+#pragma unroll
+                for (int jq = 0; jq < 8; ++jq) {
+                    const int js = 8 * h + jq;
+                    m = absmax_pair(m, pack_bf16x2(acc[it][js][0], acc[it][js][1]));
+                    m = absmax_pair(m, pack_bf16x2(acc[it][js][2], acc[it][js][3]));
+                }
+                m = absmax_fold(m);
+                m = max(m, (uint32_t)__shfl_xor((int)m, 16));
+                m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+                const TileScale ts = tile_scale(m, &g_scale_tables);
+                inv[it] = ts.inv;
+                const int64_t i = i0 + 32 * wave + 16 * it + r16;
+                if (g == 0 && i < I) Cs[i * jb_count + jb0 + h] = ts.s;
+            }
+            if (C) store_bf16(reinterpret_cast<uint16_t*>(C));
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+                const int row = 16 * it + r16;
+#pragma unroll
+                for (int jq = 0; jq < 8; ++jq) {
+                    const int js = 8 * h + jq;
+                    const uint32_t p0 = pack_bf16x2(acc[it][js][0], acc[it][js][1]);
+                    const uint32_t p1 = pack_bf16x2(acc[it][js][2], acc[it][js][3]);
+                    *reinterpret_cast<uint32_t*>(stage + row * 128 + ((jq ^ (row & 7)) << 4) + 4 * g) =
+                        cvt4_e4m3(bf16_lo(p0) * inv[it], bf16_hi(p0) * inv[it], bf16_lo(p1) * inv[it],
+                                  bf16_hi(p1) * inv[it]);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int pass = 0; pass < 4; ++pass) {
+                const int row = 8 * pass + (lane >> 3);
+                const int c = lane & 7;                    // 16-byte chunk of the 128 codes
+                const uint4 w =
+                    *reinterpret_cast<const uint4*>(stage + row * 128 + ((c ^ (row & 7)) << 4));
+                const int64_t i = i0 + 32 * wave + row;
+                if (i < I) *reinterpret_cast<uint4*>(Cq + i * J + jh + c * 16) = w;
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_wave_barrier();
+        } else if constexpr (OUT_BF16) {
+            store_bf16(reinterpret_cast<uint16_t*>(C));
+        } else {
+            float* Cf = reinterpret_cast<float*>(C) + (int64_t)blockIdx.y * I * J;
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+                const int64_t i = i0 + 32 * wave + 16 * it + r16;
+                if (i >= I) continue;
+#pragma unroll
+                for (int jq = 0; jq < 8; ++jq) {
+                    const int js = 8 * h + jq;
+                    *reinterpret_cast<float4*>(Cf + i * J + jh + 16 * jq + 4 * g) =
+                        make_float4(acc[it][js][0], acc[it][js][1], acc[it][js][2], acc[it][js][3]);
+                }
+            }
+        }
+    };
+
     // One block; MORE: the next block is loaded and staged during this one.
     // The last block runs as its own copy, so the loop body has no branch.
     auto run_block = [&](int k, auto more_tag) __attribute__((always_inline)) {
@@ -461,143 +573,22 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
                     }
                 }
             }
-            if constexpr (more) {
-                if (jp == 3) {
+            if (jp == 3) {
+                if constexpr (more) {
 #pragma unroll
                     for (int p = 0; p < 4; ++p) store_b(buf ^ 1, p);   // B of the next block, widened once
                     load_a(kb0 + k + 1);      // its A codes, in flight until the next block
+                } else if constexpr (kEarlyHalf) {
+                    out_half(std::integral_constant<int, 0>{}, buf);   // columns 0..127 are final
                 }
             }
         }
     };
     for (int k = 0; k + 1 < nkb; ++k) run_block(k, std::true_type{});
     if (nkb > 0) run_block(nkb - 1, std::false_type{});
-
-    // epilogue: lane owns C[i][j .. j+3]; split s writes its own FP32 slice
-    if constexpr (OUT_BF16) __syncthreads();   // every wave done with the LDS tiles
-    const int js_end = j_full ? 16 : 8;
-    if constexpr (QOUT) {
-        uint8_t* stage = &Bh[0][0] + wave * 16384;
-        // Scales of the row tiles (two per row: columns j0 .. j0+127 and
-        // j0+128 .. j0+255) from the BF16-rounded values.
-        float inv[2][2];
-#pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int64_t i = i0 + 32 * wave + 16 * it + r16;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                uint32_t m = 0;
-#pragma unroll
-                for (int js = 8 * t; js < 8 * t + 8; ++js) {
-                    m = absmax_pair(m, pack_bf16x2(acc[it][js][0], acc[it][js][1]));
-                    m = absmax_pair(m, pack_bf16x2(acc[it][js][2], acc[it][js][3]));
-                }
-                m = absmax_fold(m);
-                m = max(m, (uint32_t)__shfl_xor((int)m, 16));
-                m = max(m, (uint32_t)__shfl_xor((int)m, 32));
-                const TileScale ts = tile_scale(m, &g_scale_tables);
-                inv[it][t] = ts.inv;
-                if (g == 0 && i < I && (t == 0 || j_full))
-                    Cs[i * jb_count + jb0 + t] = ts.s;
-            }
-        }
-        if (C) {
-#pragma unroll
-            for (int it = 0; it < 2; ++it) {
-                const int row = 16 * it + r16;
-#pragma unroll
-                for (int js = 0; js < 16; ++js) {
-                    const int b = js * 32 + g * 8;
-                    const int phys = (((b >> 4) ^ (row & 15)) << 4) | (b & 15);
-                    *reinterpret_cast<uint2*>(stage + row * 512 + phys) =
-                        make_uint2(pack_bf16x2(acc[it][js][0], acc[it][js][1]),
-                                   pack_bf16x2(acc[it][js][2], acc[it][js][3]));
-                }
-            }
-            __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0): the wave's LDS writes
-            __builtin_amdgcn_wave_barrier();
-            uint16_t* Cb = reinterpret_cast<uint16_t*>(C);
-#pragma unroll
-            for (int pass = 0; pass < 16; ++pass) {
-                const int row = 2 * pass + (lane >> 5);
-                const int c = lane & 31;
-                const uint4 w =
-                    *reinterpret_cast<const uint4*>(stage + row * 512 + ((c ^ (row & 15)) << 4));
-                const int64_t i = i0 + 32 * wave + row;
-                if (i < I && (c < 16 || j_full))
-                    *reinterpret_cast<uint4*>(Cb + i * J + j0 + c * 8) = w;
-            }
-            __builtin_amdgcn_s_waitcnt(0xC07F);
-            __builtin_amdgcn_wave_barrier();
-        }
-#pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int row = 16 * it + r16;
-#pragma unroll
-            for (int js = 0; js < 16; ++js) {
-                const float iv = inv[it][js >> 3];
-                const uint32_t p0 = pack_bf16x2(acc[it][js][0], acc[it][js][1]);
-                const uint32_t p1 = pack_bf16x2(acc[it][js][2], acc[it][js][3]);
-                *reinterpret_cast<uint32_t*>(stage + row * 256 + ((js ^ (row & 15)) << 4) + 4 * g) =
-                    cvt4_e4m3(bf16_lo(p0) * iv, bf16_hi(p0) * iv, bf16_lo(p1) * iv, bf16_hi(p1) * iv);
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int pass = 0; pass < 8; ++pass) {
-            const int row = 4 * pass + (lane >> 4);
-            const int c = lane & 15;                           // 16-byte chunk of the 256 codes
-            const uint4 w =
-                *reinterpret_cast<const uint4*>(stage + row * 256 + ((c ^ (row & 15)) << 4));
-            const int64_t i = i0 + 32 * wave + row;
-            if (i < I && (c < 8 || j_full)) *reinterpret_cast<uint4*>(Cq + i * J + j0 + c * 16) = w;
-        }
-        return;
-    }
-    if constexpr (OUT_BF16) {
-        // Restage the wave's 32x256 BF16 patch through LDS so that it leaves
-        // as whole 512-byte rows in 16-byte stores.
-        uint8_t* stage = &Bh[0][0] + wave * 16384;
-#pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int row = 16 * it + r16;
-#pragma unroll
-            for (int js = 0; js < 16; ++js) {
-                const int b = js * 32 + g * 8;                 // byte offset in the row
-                const int phys = (((b >> 4) ^ (row & 15)) << 4) | (b & 15);
-                *reinterpret_cast<uint2*>(stage + row * 512 + phys) =
-                    make_uint2(pack_bf16x2(acc[it][js][0], acc[it][js][1]),
-                               pack_bf16x2(acc[it][js][2], acc[it][js][3]));
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(0xC07F);               // lgkmcnt(0): the wave's LDS writes
-        __builtin_amdgcn_wave_barrier();
-        uint16_t* Cb = reinterpret_cast<uint16_t*>(C);
-#pragma unroll
-        for (int pass = 0; pass < 16; ++pass) {
-            const int row = 2 * pass + (lane >> 5);
-            const int c = lane & 31;                           // 16-byte chunk of the row
-            const uint4 w =
-                *reinterpret_cast<const uint4*>(stage + row * 512 + ((c ^ (row & 15)) << 4));
-            const int64_t i = i0 + 32 * wave + row;
-            if (i < I && (c < 16 || j_full)) *reinterpret_cast<uint4*>(Cb + i * J + j0 + c * 8) = w;
-        }
-        return;
-    }
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-        const int64_t i = i0 + 32 * wave + 16 * it + r16;
-        if (i >= I) continue;
-        float* Cf = reinterpret_cast<float*>(C) + (int64_t)blockIdx.y * I * J;
-#pragma unroll
-        for (int js = 0; js < 16; ++js) {
-            const int64_t j = j0 + 16 * js + 4 * g;
-            if (js < js_end)
-                *reinterpret_cast<float4*>(Cf + i * J + j) =
-                    make_float4(acc[it][js][0], acc[it][js][1], acc[it][js][2], acc[it][js][3]);
-        }
-    }
+    const int lbuf = nkb > 0 ? (nkb - 1) & 1 : 0;
+    if (!kEarlyHalf || nkb == 0) out_half(std::integral_constant<int, 0>{}, lbuf);
+    out_half(std::integral_constant<int, 1>{}, lbuf);
 }
 
 // Sum of the split slices, in split order: out[e] = sum_s ws[s][e] (fixed order,
