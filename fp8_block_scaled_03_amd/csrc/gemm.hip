@@ -351,10 +351,6 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
     // where the codes are still in flight.
     auto store_b = [&](int buf, int p) {
         uint8_t* dst = Bh[buf];
-        // Row-scaled B (wgrad, two VALU operations per output element in the
-        // fold) runs faster with the widening fenced off from the MFMA groups
-        // around it; the block-scaled modes run faster without the fence.
-        if constexpr (MODE == kScaleRow) __builtin_amdgcn_sched_barrier(0);
         uint4 w = bn[p];
         asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
         *reinterpret_cast<v8h*>(dst + f16_frag_off(brow, 8 * bh + 2 * p)) = widen8(w.x, w.y);
