@@ -248,7 +248,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bs_fp8_kernel(
 // (widening and the scale fold) stays well below the MFMA time.
 // Per block: the next block's B codes are requested at the top; after the
 // fourth of eight MFMA groups they are widened and stored into the other FP16
-// buffer in one burst, and the next block's A codes are requested.
+// buffer in one burst, and the next block's A codes are requested.  Each MFMA
+// group's B fragments are read from LDS one group ahead.  The epilogue works
+// in two 128-column halves; in the block-scaled modes the first leaves
+// during the last block, once its columns are final.
 // The FP16 B tile is stored in fragment order: the 16 bytes that lane l reads
 // for MFMA chunk c of B subtile js sit at ((4 js + c) * 64 + l) * 16, so every
 // fragment read is one contiguous 1 KB block (gfx950's LDS serves those
