@@ -36,14 +36,24 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and blank lines (a comment edit does not
+    change a kernel).  String literals in these sources hold no comment
+    markers."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+
+
 def source_digest(kind: str) -> str:
-    """Digest of the sources a kernel kind is built from (counter records
-    taken on other sources are stale)."""
+    """Digest of the code (comments stripped) of the sources a kernel kind is
+    built from: counter records taken on other code are stale."""
     import hashlib
     h = hashlib.sha256()
     for fn in KERNEL_SOURCES["gemm" if kind.startswith("gemm") else "quant"]:
-        with open(os.path.join(ROOT, "fp8_block_scaled_03_amd", "csrc", fn), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "fp8_block_scaled_03_amd", "csrc", fn), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
