@@ -249,9 +249,11 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bs_fp8_kernel(
 // Per block: the next block's B codes are requested at the top; after the
 // fourth of eight MFMA groups they are widened and stored into the other FP16
 // buffer in one burst, and the next block's A codes are requested.  Each MFMA
-// group's B fragments are read from LDS one group ahead.  The epilogue works
-// in two 128-column halves; in the block-scaled modes the first leaves
-// during the last block, once its columns are final.
+// group's B fragments are read from LDS one group ahead.  In the block-scaled
+// modes each group's partial sums are folded one group late, while the next
+// group's MFMAs run.  The epilogue works in two 128-column halves; in the
+// block-scaled modes the first leaves during the last block, once its columns
+// are final.
 // The FP16 B tile is stored in fragment order: the 16 bytes that lane l reads
 // for MFMA chunk c of B subtile js sit at ((4 js + c) * 64 + l) * 16, so every
 // fragment read is one contiguous 1 KB block (gfx950's LDS serves those
@@ -388,6 +390,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
     const bool j_full = j0 + kBigN <= J;             // else only the first 128 columns exist
     // The row-scaled (FP32) instantiation has no registers for the early half.
     constexpr bool kEarlyHalf = MODE != kScaleRow;
+    constexpr bool kLagFold = MODE != kScaleRow && !QOUT;
     auto out_half = [&](auto h_tag, int lbuf) __attribute__((always_inline)) {
         constexpr int h = decltype(h_tag)::value;
         if (h == 1 && !j_full) return;
@@ -526,6 +529,39 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
         for (int t = 0; t < kAhead; ++t)
 #pragma unroll
             for (int jj = 0; jj < JJ; ++jj) bq[t][jj] = frag(t, jj);
+        // Fold one MFMA group's partials (B subtiles JJ jq .. JJ jq + JJ - 1) into acc.
+        auto fold = [&](v4f (&q)[JJ][2], int jq) __attribute__((always_inline)) {
+#pragma unroll
+            for (int jj = 0; jj < JJ; ++jj) {
+                const int js = JJ * jq + jj;
+                if (MODE != kScaleRow) {
+#pragma unroll
+                    for (int it = 0; it < 2; ++it) {
+                        const float cs = js < 8 ? cs0[it] : cs1[it];
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            acc[it][js][v] = __builtin_fmaf(q[jj][it][v], cs, acc[it][js][v]);
+                    }
+                } else {
+                    // (P * sB(j)) * sA(i): the column scale is applied in place,
+                    // so the fold needs no registers for scale products.
+                    const float4 sb = *reinterpret_cast<const float4*>(&sBs[buf][16 * js + 4 * g]);
+#pragma unroll
+                    for (int it = 0; it < 2; ++it) {
+                        acc[it][js][0] = __builtin_fmaf(q[jj][it][0] * sb.x, sa[it], acc[it][js][0]);
+                        acc[it][js][1] = __builtin_fmaf(q[jj][it][1] * sb.y, sa[it], acc[it][js][1]);
+                        acc[it][js][2] = __builtin_fmaf(q[jj][it][2] * sb.z, sa[it], acc[it][js][2]);
+                        acc[it][js][3] = __builtin_fmaf(q[jj][it][3] * sb.w, sa[it], acc[it][js][3]);
+                    }
+                }
+            }
+        };
+        // kLagFold: group jp's partials are folded while group jp + 1's MFMAs
+        // run, so the FMAs fill the matrix core's issue gaps instead of waiting
+        // for the group's last MFMA.  That needs a second set of partials (16
+        // registers), which only the block-scaled instantiations without the
+        // quantizing epilogue have; the others fold each group right after it.
+        v4f pl[JJ][2];
 #pragma unroll
         for (int jp = 0; jp < 16 / JJ; ++jp) {
             v4f p[JJ][2];
@@ -548,40 +584,27 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
                         p[jj][it] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bq[t % kSets][jj], af[it][c],
                                                                             p[jj][it], 0, 0, 0);
             }
+            if constexpr (kLagFold) {
+                if (jp > 0) fold(pl, jp - 1);
 #pragma unroll
-            for (int jj = 0; jj < JJ; ++jj) {
-                const int js = JJ * jp + jj;
-                if (MODE != kScaleRow) {
+                for (int jj = 0; jj < JJ; ++jj)
 #pragma unroll
-                    for (int it = 0; it < 2; ++it) {
-                        const float cs = js < 8 ? cs0[it] : cs1[it];
-#pragma unroll
-                        for (int v = 0; v < 4; ++v)
-                            acc[it][js][v] = __builtin_fmaf(p[jj][it][v], cs, acc[it][js][v]);
-                    }
-                } else {
-                    // (P * sB(j)) * sA(i): the column scale is applied in place,
-                    // so the fold needs no registers for scale products.
-                    const float4 sb = *reinterpret_cast<const float4*>(&sBs[buf][16 * js + 4 * g]);
-#pragma unroll
-                    for (int it = 0; it < 2; ++it) {
-                        acc[it][js][0] = __builtin_fmaf(p[jj][it][0] * sb.x, sa[it], acc[it][js][0]);
-                        acc[it][js][1] = __builtin_fmaf(p[jj][it][1] * sb.y, sa[it], acc[it][js][1]);
-                        acc[it][js][2] = __builtin_fmaf(p[jj][it][2] * sb.z, sa[it], acc[it][js][2]);
-                        acc[it][js][3] = __builtin_fmaf(p[jj][it][3] * sb.w, sa[it], acc[it][js][3]);
-                    }
-                }
+                    for (int it = 0; it < 2; ++it) pl[jj][it] = p[jj][it];
+            } else {
+                fold(p, jp);
             }
-            if (jp == 3) {
-                if constexpr (more) {
+            if constexpr (more) {
+                if (jp == 3) {
 #pragma unroll
                     for (int p = 0; p < 4; ++p) store_b(buf ^ 1, p);   // B of the next block, widened once
                     load_a(kb0 + k + 1);      // its A codes, in flight until the next block
-                } else if constexpr (kEarlyHalf) {
-                    out_half(std::integral_constant<int, 0>{}, buf);   // columns 0..127 are final
                 }
+            } else if constexpr (kEarlyHalf) {
+                // columns 0..127 (groups 0..3) are final once group 3 is folded
+                if (jp == (kLagFold ? 4 : 3)) out_half(std::integral_constant<int, 0>{}, buf);
             }
         }
+        if constexpr (kLagFold) fold(pl, 16 / JJ - 1);
     };
     for (int k = 0; k + 1 < nkb; ++k) run_block(k, std::true_type{});
     if (nkb > 0) run_block(nkb - 1, std::false_type{});
