@@ -157,6 +157,28 @@ def test_wgrad_split_matches_unsplit_bitwise_and_oracle():
     check_f32(c, ref, da, db, "wgrad unsplit")
 
 
+def test_wgrad_split_reuses_any_workspace():
+    """Nothing carries over in the split workspace: one full of garbage,
+    reused for a second call, or fresh gives the same bits."""
+    M, N, K = 4096, 384, 640          # six tiles (ragged in both directions), eight splits
+    dyb = inputs.student_t((34, M, N), (M, N), 3.0, 1e-3)
+    xb = inputs.random_bits((35, M, K), (M, K), "wide")
+    dy, x = to_dev_bf16(dyb), to_dev_bf16(xb)
+    dytq, dyts = fp8.fp8_quantize_transposed(dy)
+    xtq, xts = fp8.fp8_quantize_transposed(x)
+    nbytes = fp8.fp8_gemm_wgrad_workspace_bytes(M, N, K)
+    _say(f"wgrad {M}x{N}x{K} workspace {nbytes} bytes")
+    assert nbytes > 0
+    ws = torch.full((nbytes,), 255, dtype=torch.uint8, device="cuda")
+    outs = [fp8.fp8_gemm_wgrad(dytq, dyts, xtq, xts, workspace=ws) for _ in range(2)]
+    outs.append(fp8.fp8_gemm_wgrad(dytq, dyts, xtq, xts, workspace="auto"))
+    torch.cuda.synchronize()
+    bits = [to_np(o).view(np.uint32) for o in outs]
+    assert np.array_equal(bits[0], bits[1]) and np.array_equal(bits[0], bits[2])
+    ref, a, b = ref_wgrad(dyb, xb)
+    check_f32(to_np(outs[0]), ref, a, b, "wgrad split, reused workspace")
+
+
 def test_gemm_special_tiles(kernel):
     """Zero tiles, negative-zero tiles, subnormal-scale tiles and exact E4M3
     grids in both operands."""
