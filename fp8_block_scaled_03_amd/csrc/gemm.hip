@@ -15,8 +15,10 @@
 // MFMA accumulates its products at FP32 precision, so the codes are widened
 // to FP16 (v_cvt_scalef32_pk_f16_fp8, scale 1) and contracted with
 // v_mfma_f32_16x16x32_f16: four chained instructions give P for one 128-wide
-// block in FP32, which is folded into the FP32 accumulator with one FMA per
-// output element (acc += P * sA*sB).
+// block in FP32, which is folded into the FP32 accumulator: acc += P * sA*sB,
+// one FMA per output element where sA*sB is one product per row and block
+// (fprop, dgrad), a multiply and an FMA where both scales vary along the
+// tile (wgrad).
 //
 // Two kernels share that arithmetic:
 //   gemm_bs_fp8_kernel      workgroup tile 128 (i) x 128 (j) x 128 (k), four
@@ -363,8 +365,8 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
         if (MODE == kScaleRow && p == 0) sBs[buf][brow] = sbrn;   // both halves of the row write it
     };
 
-    // B subtiles per MFMA group: two (four independent chains) where the fold
-    // is one FMA per element, one where it also needs a scale product.
+    // B subtiles per MFMA group: two, so a group is four independent chains
+    // of four MFMAs (two A subtiles x two B subtiles), in every mode.
     constexpr int JJ = 2;
     v4f acc[2][16];
 #pragma unroll
