@@ -384,6 +384,23 @@ def _time_events(torch, fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
+def mfma_ceiling(torch, fp8, reps=5):
+    """Attainable FP16 MFMA rate of this GPU in TFLOP/s: the library's MFMA-only
+    diagnostic kernel (8 workgroups of 256 threads per CU, ~3 ms a launch),
+    best of reps, after checking its exact output."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters, v = 8 * cus, 400, 0.125
+    flop = blocks * 4 * iters * 128 * 16384
+    out = fp8.fp8bs_mfma_rate(blocks, iters, v)
+    torch.cuda.synchronize()
+    expect = 16384 * v * v * iters
+    if not bool((out == expect).all()):
+        raise RuntimeError("MFMA-rate kernel returned wrong values")
+    best = min(_time_events(torch, lambda: fp8.fp8bs_mfma_rate(blocks, iters, v, out=out), 1)
+               for _ in range(reps))
+    return flop / (best / 1e3) / 1e12
+
+
 def bf16_comparison(torch, fp8, cfg, fp8_ms_per_layer, reps=5):
     """The 12 GEMMs of one layer in TN form on BF16 operands: this library's
     BF16 kernel and torch's BF16 matmul (the vendor BLAS), against the FP8
@@ -573,6 +590,12 @@ def main():
                  "accumulation parity") if dom_is_gemm else "",
     }
 
+    if dom_is_gemm:
+        # the same kernel's rate against what the matrix cores sustain on this
+        # GPU at the clock they hold under load (measured after the timed steps)
+        ceiling = mfma_ceiling(torch, fp8)
+        roofline["peak_at_clock"] = round(ceiling, 1)
+        roofline["frac_at_clock"] = round(d["rate"] / ceiling, 4)
     rec = recorded_traffic(dom)
     if rec:
         roofline["traffic"] = rec["bytes_per_launch"]

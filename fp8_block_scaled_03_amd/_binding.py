@@ -39,6 +39,7 @@ SIGNATURES = {
     "fp8_gemm_wgrad_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64]),
     "bf16_gemm_tn": (_INT, [_P, _P, _P, _INT, _I64, _I64, _I64, _P]),
     "fp8_encode_e4m3": (_INT, [_P, _I64, _P, _P]),
+    "fp8bs_mfma_rate": (_INT, [_P, _I64, _INT, ctypes.c_float, _P]),
     "fp8bs_status_string": (ctypes.c_char_p, [_INT]),
     "fp8bs_version": (_INT, []),
 }
@@ -269,6 +270,17 @@ def fp8_encode_e4m3(x: torch.Tensor, q=None, stream=None):
     _check("fp8_encode_e4m3", capi().fp8_encode_e4m3(_ptr(x), x.numel(), _ptr(q),
                                                      _stream(x, stream)))
     return q
+
+
+def fp8bs_mfma_rate(blocks: int, iters: int, v: float = 0.125, out=None, device="cuda",
+                    stream=None):
+    """Diagnostic: MFMA-only work of blocks x 256 threads (blocks * 4 * iters *
+    128 * 16384 flop); returns the float32 [blocks * 256] results, each
+    16384 * v^2 * iters."""
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=device) if out is None else out
+    _check("fp8bs_mfma_rate", capi().fp8bs_mfma_rate(_ptr(out), blocks, iters, v,
+                                                     _stream(out, stream)))
+    return out
 
 
 def fp8bs_status_string(status: int) -> str:

@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstdint>
 #include <cstring>
 #include <mutex>
 
@@ -63,7 +64,7 @@ fp8bs_status launched(hipError_t e) { return e == hipSuccess ? FP8BS_OK : FP8BS_
 
 extern "C" {
 
-int fp8bs_version(void) { return 100; }
+int fp8bs_version(void) { return 200; }
 
 const char* fp8bs_status_string(fp8bs_status status) {
     switch (status) {
@@ -234,6 +235,16 @@ fp8bs_status fp8_encode_e4m3(const float* x, int64_t n, uint8_t* q, fp8bs_stream
     int cus;
     FP8BS_TRY(check_device(&cus));
     return launched(fp8bs::launch_encode_e4m3(x, n, q, stream));
+}
+
+fp8bs_status fp8bs_mfma_rate(float* out, int64_t blocks, int iters, float v,
+                             fp8bs_stream_t stream) {
+    if (blocks < 0 || blocks > INT32_MAX || iters < 0) return FP8BS_ERR_SHAPE;
+    FP8BS_TRY(check_ptr(out, blocks == 0, 16));
+    if (blocks == 0) return FP8BS_OK;
+    int cus;
+    FP8BS_TRY(check_device(&cus));
+    return launched(fp8bs::launch_mfma_rate(out, blocks, iters, v, stream));
 }
 
 }  // extern "C"

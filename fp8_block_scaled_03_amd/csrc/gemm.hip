@@ -788,4 +788,38 @@ hipError_t launch_gemm(ScaleMode mode, const uint8_t* A, const float* sA, const 
     return hipErrorInvalidValue;
 }
 
+// Attainable FP16 MFMA rate on this device: every wave issues iters x 16
+// rounds of eight independent v_mfma_f32_16x16x32_f16 chains and touches
+// memory only to store its result, so the kernel's time is the matrix cores'
+// own, at the clock they hold under MFMA load.  (The compiler adds about 56
+// accumulator-register moves per 128 MFMAs at the loop edge; they run on the
+// VALU beside the other waves' MFMAs.)  With every operand element equal to
+// v, each output element of a chain grows by 32 v^2 per instruction, and each
+// thread stores the sum of its 32 accumulator elements: 16384 v^2 iters.
+__global__ __launch_bounds__(256) void mfma_rate_kernel(float* __restrict__ out, int iters,
+                                                        float v) {
+    const _Float16 h = (_Float16)v;
+    const v8h a = {h, h, h, h, h, h, h, h};
+    v4f acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, a, acc[j], 0, 0, 0);
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sum += (acc[j][0] + acc[j][1]) + (acc[j][2] + acc[j][3]);
+    out[(int64_t)blockIdx.x * 256 + threadIdx.x] = sum;
+}
+
+hipError_t launch_mfma_rate(float* out, int64_t blocks, int iters, float v, hipStream_t stream) {
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(mfma_rate_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, out, iters, v);
+    return hipGetLastError();
+}
+
 }  // namespace fp8bs

@@ -44,4 +44,7 @@ hipError_t launch_gemm_quantized(ScaleMode mode, const uint8_t* A, const float* 
 hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* B, void* C, bool out_bf16,
                             int64_t I, int64_t J, int64_t K, hipStream_t stream);
 
+// Diagnostic: blocks x 256 threads of MFMA-only work (see mfma_rate_kernel).
+hipError_t launch_mfma_rate(float* out, int64_t blocks, int iters, float v, hipStream_t stream);
+
 }  // namespace fp8bs

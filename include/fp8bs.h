@@ -214,6 +214,21 @@ fp8bs_status bf16_gemm_tn(const uint16_t* a, const uint16_t* b, void* c, fp8bs_o
  */
 fp8bs_status fp8_encode_e4m3(const float* x, int64_t n, uint8_t* q, fp8bs_stream_t stream);
 
+/*
+ * Diagnostic, outside the FP8 path: the attainable FP16 MFMA rate, against
+ * which a GEMM's rate can be priced at the clock the chip actually holds
+ * under matrix load (the contraction runs on v_mfma_f32_16x16x32_f16).
+ * Runs `blocks` workgroups of 256 threads; every wave issues iters x 128 of
+ * those instructions (16384 flop each) on operands whose elements all equal
+ * v, with no memory traffic, and each thread stores 16384 * v^2 * iters
+ * (exact while that is below 2^24).  Work: blocks * 4 * iters * 128 * 16384
+ * flop.
+ *   out f32 [blocks * 256], 16-byte aligned device memory, caller-owned.
+ *   blocks >= 0 (0 does nothing), iters >= 0; FP8BS_ERR_SHAPE otherwise.
+ * Asynchronous on stream: time it with events recorded on the same stream.
+ */
+fp8bs_status fp8bs_mfma_rate(float* out, int64_t blocks, int iters, float v, fp8bs_stream_t stream);
+
 /* Static string naming a status (never NULL). */
 const char* fp8bs_status_string(fp8bs_status status);
 

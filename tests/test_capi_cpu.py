@@ -30,14 +30,14 @@ def L():
 
 def test_exports_every_header_symbol(L):
     names = header_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(B.SIGNATURES)
 
 
 def test_version_and_status_strings(L):
-    assert L.fp8bs_version() == 100
+    assert L.fp8bs_version() == 200
     for st in range(8):
         s = L.fp8bs_status_string(st)
         assert s and isinstance(s, bytes)
@@ -133,6 +133,16 @@ def test_bf16_gemm_argument_errors(L):
     assert f(A16, MIS, A16, 1, 4, 128, 128, None) == ALIGN
     assert f(A16, A16, A16 + 8, 0, 4, 128, 128, None) == ALIGN
     assert f(None, None, None, 1, 0, 128, 128, None) == OK
+
+
+def test_mfma_rate_argument_errors(L):
+    f = L.fp8bs_mfma_rate
+    assert f(A16, -1, 10, 0.125, None) == SHAPE
+    assert f(A16, 4, -1, 0.125, None) == SHAPE
+    assert f(A16, 1 << 31, 10, 0.125, None) == SHAPE
+    assert f(None, 4, 10, 0.125, None) == NULL
+    assert f(MIS, 4, 10, 0.125, None) == ALIGN
+    assert f(None, 0, 10, 0.125, None) == OK
 
 
 def test_binding_names_match_c_names():
