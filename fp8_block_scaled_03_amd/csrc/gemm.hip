@@ -378,7 +378,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
         load_b(kb0);
         load_a(kb0);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) store_b(0, p);
+        for (int part = 0; part < 4; ++part) store_b(0, part);
     }
     // Output half h (columns j0 + 128h .. +127, i.e. B subtiles 8h .. 8h+7)
     // of the tile: lane owns C[i][j .. j+3]; split s writes its own FP32
@@ -598,7 +598,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
             if constexpr (more) {
                 if (jp == 3) {
 #pragma unroll
-                    for (int p = 0; p < 4; ++p) store_b(buf ^ 1, p);   // B of the next block, widened once
+                    for (int part = 0; part < 4; ++part) store_b(buf ^ 1, part);   // B of the next block, widened once
                     load_a(kb0 + k + 1);      // its A codes, in flight until the next block
                 }
             } else if constexpr (kEarlyHalf) {
