@@ -1,0 +1,85 @@
+"""Every entry point enqueues on the stream it is given (the caller's current
+stream through the binding).  On a side stream, a long spin kernel is queued
+first and the inputs are overwritten after it; a call that ran anywhere but
+behind them would read the old inputs, so its outputs would differ from the
+same call made afterwards on the default stream with the new inputs."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_block_scaled_03_amd as fp8
+from fp8_block_scaled_03_amd import inputs
+from helpers import to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+SPIN_CYCLES = 50_000_000        # a few tens of ms of device time
+
+
+def _bits(t):
+    return t.view(torch.uint8) if t.element_size() == 1 else t.view(torch.int32) if t.element_size() == 4 else t.view(torch.int16)
+
+
+def _same(a, b):
+    return torch.equal(_bits(a.contiguous()), _bits(b.contiguous()))
+
+
+def test_quantizers_run_on_the_callers_stream():
+    M, C = 256, 512
+    old = to_dev_bf16(inputs.normal((40,), (M, C)))
+    new = to_dev_bf16(inputs.student_t((41,), (M, C), 3.0, 0.5))
+    x = old.clone()
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    print("quantizers on a side stream", flush=True)
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(SPIN_CYCLES)
+        x.copy_(new)
+        got = (fp8.fp8_quantize_rowtile(x), fp8.fp8_quantize_dual(x),
+               fp8.fp8_quantize_transposed(x), fp8.fp8_quantize_block(x))
+    side.synchronize()
+    want = (fp8.fp8_quantize_rowtile(new), fp8.fp8_quantize_dual(new),
+            fp8.fp8_quantize_transposed(new), fp8.fp8_quantize_block(new))
+    torch.cuda.synchronize()
+    for g, w in zip(got, want):
+        for a, b in zip(g, w):
+            assert _same(a, b)
+
+
+def test_gemms_run_on_the_callers_stream():
+    M, N, K = 512, 384, 640
+    xb = inputs.normal((42,), (M, K))
+    wb = inputs.normal((43,), (N, K), 0.02)
+    dyb = inputs.student_t((44,), (M, N), 3.0, 1e-3)
+    x, w, dy = to_dev_bf16(xb), to_dev_bf16(wb), to_dev_bf16(dyb)
+    xq, xs, xtq, xts = fp8.fp8_quantize_dual(x)
+    wq, wqt, ws = fp8.fp8_quantize_block(w)
+    dyq, dys, dytq, dyts = fp8.fp8_quantize_dual(dy)
+    srcs = [xq, xs, xtq, xts, wq, wqt, ws, dyq, dys, dytq, dyts, x, w]
+    live = [torch.zeros_like(t) for t in srcs]      # what the calls read: zeros until the copy
+    lxq, lxs, lxtq, lxts, lwq, lwqt, lws, ldyq, ldys, ldytq, ldyts, lx, lw = live
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    print("GEMMs on a side stream", flush=True)
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(SPIN_CYCLES)
+        for dst, src in zip(live, srcs):
+            dst.copy_(src)
+        got = (fp8.fp8_gemm_fprop(lxq, lxs, lwq, lws),
+               fp8.fp8_gemm_dgrad(ldyq, ldys, lwqt, lws),
+               fp8.fp8_gemm_wgrad(ldytq, ldyts, lxtq, lxts, workspace="auto"),
+               fp8.fp8_gemm_dgrad_quantized(ldyq, ldys, lwqt, lws),
+               fp8.bf16_gemm_tn(lx, lw))
+    side.synchronize()
+    want = (fp8.fp8_gemm_fprop(xq, xs, wq, ws),
+            fp8.fp8_gemm_dgrad(dyq, dys, wqt, ws),
+            fp8.fp8_gemm_wgrad(dytq, dyts, xtq, xts, workspace="auto"),
+            fp8.fp8_gemm_dgrad_quantized(dyq, dys, wqt, ws),
+            fp8.bf16_gemm_tn(x, w))
+    torch.cuda.synchronize()
+    for g, w_ in zip(got, want):
+        g = g if isinstance(g, tuple) else (g,)
+        w_ = w_ if isinstance(w_, tuple) else (w_,)
+        for a, b in zip(g, w_):
+            assert _same(a, b)
+    assert np.isfinite(got[0].float().cpu().numpy()).all()
