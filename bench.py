@@ -325,11 +325,14 @@ def run_step(ops, events=None):
         events[len(ops)].record()
 
 
-def cpu_baseline(fraction: int):
+def cpu_baseline(fraction: int, gpu=None):
     """The oracle, as it stands, on layer 0 of the same workload: each of the
     12 GEMMs on 1/fraction of its output rows, with the quantization those
     rows need (row tiles of the sampled rows, whole weight blocks, token-axis
-    tiles of the sampled gradient channels and of the whole other operand)."""
+    tiles of the sampled gradient channels and of the whole other operand).
+    With gpu (host copies of the GPU's layer-0 codes, scales and outputs, see
+    gpu_layer0), the oracle's results are then compared with them, outside
+    the timed part: (baseline, parity)."""
     import numpy as np
 
     import oracle
@@ -339,6 +342,7 @@ def cpu_baseline(fraction: int):
     cores = len(os.sched_getaffinity(0))
     host = {n: inputs.tensor("linear_set", n, layer=0) for n in cfg.tensors}
     flops = 0
+    results = []
     t0 = time.perf_counter()
     for g in cfg.gemms:
         a, b = host[g.a], host[g.b]
@@ -348,23 +352,96 @@ def cpu_baseline(fraction: int):
             wq, wqt, ws = oracle.quantize_block(b, with_transpose=(g.kind == "dgrad"),
                                                 threads=cores)
             if g.kind == "fprop":
-                oracle.gemm_fprop(aq, as_, wq, ws, threads=cores)
-                flops += 2 * len(rows) * g.N * g.K
+                y = oracle.gemm_fprop(aq, as_, wq, ws, threads=cores)
             else:
-                oracle.gemm_dgrad(aq, as_, wqt, ws, threads=cores)
-                flops += 2 * len(rows) * g.N * g.K
+                y = oracle.gemm_dgrad(aq, as_, wqt, ws, threads=cores)
+            flops += 2 * len(rows) * g.N * g.K
+            results.append((g, rows, (aq, as_), (wq, wqt, ws), y))
         else:
             rows = np.arange(0, g.N, fraction)
             dq, ds = oracle.quantize_transposed(np.ascontiguousarray(a[:, rows]), threads=cores)
             xq, xs = oracle.quantize_transposed(b, threads=cores)
-            oracle.gemm_wgrad(dq, ds, xq, xs, threads=cores)
+            y = oracle.gemm_wgrad(dq, ds, xq, xs, threads=cores)
             flops += 2 * len(rows) * g.K * g.M
+            results.append((g, rows, (dq, ds), (xq, xs), y))
     secs = time.perf_counter() - t0
-    return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"layer 0 of the 28-layer linear set: all 12 GEMMs on 1/{fraction} of "
-                      f"their output rows ({flops / 1e9:.1f} GFLOP) plus the quantization those "
-                      f"rows need; {secs:.1f} s wall"}
+    baseline = {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+                "kind": "oracle",
+                "sample": f"layer 0 of the 28-layer linear set: all 12 GEMMs on 1/{fraction} of "
+                          f"their output rows ({flops / 1e9:.1f} GFLOP) plus the quantization "
+                          f"those rows need; {secs:.1f} s wall"}
+    if gpu is None:
+        return baseline, None
+    return baseline, _parity_against_oracle(np, oracle, gpu, results)
+
+
+def _parity_against_oracle(np, oracle, gpu, results):
+    """Codes and scales must match bit for bit; FP32 outputs relF <= 1e-5 and
+    |err| <= 1e-4 ||a_i|| ||b_j|| (dequantized contraction vectors); BF16
+    outputs within one BF16 ulp of the rounded oracle value, or within that
+    bound plus half an ulp."""
+    codes_ok = True
+    gemms = {}
+    for g, rows, qa, qb, y in results:
+        if g.kind in ("fprop", "dgrad"):
+            rq, rs = gpu["rq"][g.a]
+            codes_ok &= np.array_equal(rq[rows], qa[0]) and np.array_equal(
+                rs[rows].view(np.uint32), qa[1].view(np.uint32))
+            wq, wqt, ws = gpu["wq"][g.b]
+            codes_ok &= np.array_equal(wq, qb[0]) and np.array_equal(
+                ws.view(np.uint32), qb[2].view(np.uint32))
+            a_deq = oracle.dequantize_rows(*qa)
+            w_deq = oracle.dequantize_block(qb[0], qb[2])
+            if g.kind == "dgrad":
+                codes_ok &= np.array_equal(wqt, qb[1])
+                w_deq = np.ascontiguousarray(w_deq.T)
+            out = gpu["out"][g.name][rows]
+            ref_bits = oracle.f32_to_bf16(y)
+            got = oracle.bf16_to_f32(out).astype(np.float64)
+            ref = oracle.bf16_to_f32(ref_bits).astype(np.float64)
+            mag = np.maximum(np.abs(ref), np.finfo(np.float32).tiny)
+            ulp = np.exp2(np.floor(np.log2(mag)) - 7)
+            bound = 1e-4 * np.outer(np.linalg.norm(a_deq, axis=1), np.linalg.norm(w_deq, axis=1))
+            err = np.abs(got - ref)
+            ok = (err <= ulp) | (err <= bound + 0.5 * ulp)
+            gemms[g.name] = {"out": "bf16", "elements": int(ok.size),
+                             "within_gate": bool(ok.all()),
+                             "relF_vs_fp32_oracle": float(f"{oracle.rel_frobenius(got, y):.3e}")}
+        else:
+            tq, ts = gpu["tq"][g.a]
+            codes_ok &= np.array_equal(tq[rows], qa[0]) and np.array_equal(
+                ts[rows].view(np.uint32), qa[1].view(np.uint32))
+            xq, xs = gpu["tq"][g.b]
+            codes_ok &= np.array_equal(xq, qb[0]) and np.array_equal(
+                xs.view(np.uint32), qb[1].view(np.uint32))
+            out = gpu["out"][g.name][rows]
+            rel = oracle.rel_frobenius(out, y)
+            ratio = oracle.elementwise_bound_ratio(out, y, oracle.dequantize_rows(*qa),
+                                                   oracle.dequantize_rows(*qb), 1e-4)
+            gemms[g.name] = {"out": "f32", "elements": int(out.size),
+                             "within_gate": bool(rel <= 1e-5 and ratio <= 1.0),
+                             "relF": float(f"{rel:.3e}"),
+                             "max_err_over_bound": float(f"{ratio:.3e}")}
+    return {"layer": 0, "codes_and_scales_bit_exact": bool(codes_ok),
+            "all_gemms_within_gate": all(v["within_gate"] for v in gemms.values()),
+            "gemms": gemms}
+
+
+def gpu_layer0(torch, plan, ops):
+    """Run layer 0's launches of the step once more and copy what they wrote
+    (codes, scales, outputs) to the host, for the oracle comparison."""
+    per_layer = len(ops) // plan.cfg.layers
+    run_step(ops[:per_layer])
+    torch.cuda.synchronize()
+
+    def host(t):
+        t = t.cpu()
+        return t.view(torch.int16).numpy().view("uint16") if t.dtype == torch.bfloat16 else t.numpy()
+
+    return {"rq": {n: tuple(host(t) for t in v) for n, v in plan.rq.items()},
+            "tq": {n: tuple(host(t) for t in v) for n, v in plan.tq.items()},
+            "wq": {n: tuple(host(t) for t in v) for n, v in plan.wq.items()},
+            "out": {n: host(t) for n, t in plan.out.items()}}
 
 
 LAYER_LINEARS = [("qkv", 2048, 4096), ("o", 2048, 2048), ("gate_up", 2048, 12288),
@@ -624,6 +701,8 @@ def main():
     }
     if standalone:
         result["kernels_outside_step"] = kind_summary(standalone, 1)
+    # the GPU's own layer-0 results, compared with the oracle's in the cpu_baseline leg
+    layer0 = None if args.no_cpu_baseline else gpu_layer0(torch, plan, ops)
     if not args.no_next_rows:
         cfg_obj, cfg_layers = plan.cfg, plan.cfg.layers
         del plan, ops, events
@@ -634,7 +713,7 @@ def main():
                                **dgrad_epilogue_quantization(torch, fp8, cfg_obj),
                                **fp8_linear_comparison(torch, fp8)}
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(args.cpu_fraction)
+        result["cpu_baseline"], result["parity_sample"] = cpu_baseline(args.cpu_fraction, layer0)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
