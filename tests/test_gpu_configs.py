@@ -3,8 +3,8 @@ benchmark launches them (activations and gradients through the dual-axis
 quantizer, weights through the block quantizer, wgrad with its split-K
 workspace), compared with the oracle on sampled output rows (row tiles and
 weight blocks are local, so the oracle quantizes only what the sampled rows
-need).  Quantizer outputs of these tensors are compared in full by
-test_gpu_quant."""
+need), and for the three mid-size configurations on every output element.  Quantizer
+outputs of these tensors are compared in full by test_gpu_quant."""
 import numpy as np
 import pytest
 import torch
@@ -92,3 +92,18 @@ def test_linear_set_layer_sampled(layer):
         n_rows = g.M if g.kind != "wgrad" else g.N
         rows = sample_rows(n_rows, k=16, seed=layer)
         gemm_case(g.kind, cache[g.a], cache[g.b], g.out, rows)
+
+
+@pytest.mark.parametrize("cfg", ["qkv", "mlp", "down_bwd"])
+def test_config_gemms_every_element(cfg):
+    """Every output element, not a sample, of the QKV fprop (8192 x 4096 x
+    2048), the MLP pair (gate/up 8192 x 12288 x 2048, down 8192 x 2048 x 6144)
+    and the down-projection backward (dgrad and wgrad, 8192 tokens, 2048 x
+    6144) against the oracle."""
+    c = inputs.CONFIGS[cfg]
+    for g in c.gemms:
+        _say(f"config {cfg} {g.name} M={g.M} N={g.N} K={g.K} out={g.out}: every element")
+        abits = inputs.tensor(cfg, g.a)
+        bbits = inputs.tensor(cfg, g.b)
+        n_rows = g.M if g.kind != "wgrad" else g.N
+        gemm_case(g.kind, abits, bbits, g.out, np.arange(n_rows))
