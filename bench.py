@@ -122,10 +122,25 @@ def summarize_rocprof(d: str) -> None:
             a["dispatches"].add(r["Dispatch_Id"])
             a[r["Counter_Name"]] = a.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
         print(f"# {os.path.relpath(path, d)} (per-dispatch averages)")
+        ratios = []
         for (name, grid), a in sorted(agg.items()):
             n = len(a.pop("dispatches"))
             vals = " ".join(f"{c}={v / n:.6g}" for c, v in sorted(a.items()))
             print(f"{name[:64]:64s} grid={grid:>9s} n={n:4d} {vals}")
+            r = []
+            if a.get("SQ_BUSY_CU_CYCLES") and "SQ_VALU_MFMA_BUSY_CYCLES" in a:
+                r.append(f"mfma_busy={a['SQ_VALU_MFMA_BUSY_CYCLES'] / (4 * a['SQ_BUSY_CU_CYCLES']):.3f}")
+            if a.get("SQ_LDS_IDX_ACTIVE") and "SQ_LDS_BANK_CONFLICT" in a:
+                r.append(f"lds_conflict={a['SQ_LDS_BANK_CONFLICT'] / a['SQ_LDS_IDX_ACTIVE']:.3f}")
+            if a.get("SQ_WAVE_CYCLES") and "SQ_WAIT_INST_ANY" in a:
+                r.append(f"wave_wait={a['SQ_WAIT_INST_ANY'] / a['SQ_WAVE_CYCLES']:.3f}")
+            if r:
+                ratios.append(f"{name[:64]:64s} grid={grid:>9s} " + " ".join(r))
+        if ratios:
+            print("# ratios: mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (4 SIMDs x SQ_BUSY_CU_CYCLES); "
+                  "lds_conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; "
+                  "wave_wait = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES")
+            print("\n".join(ratios))
 
 
 def parse():

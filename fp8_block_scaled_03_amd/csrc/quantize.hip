@@ -174,8 +174,10 @@ hipError_t launch_quant_block(const uint16_t* w, int64_t N, int64_t K, uint8_t* 
 //   Rows: thread t holds chunk t%16 (8 channels) of rows 32q + t/16, q = 0..3;
 //     the 16 lanes of a row reduce its amax with four lane swaps.
 //   Columns: the tile is copied to LDS with token r stored at physical row
-//     8*(r%16) + r/16 and a 72-dword row stride, so that both the 16-byte row
-//     writes and the column reads below touch 64 distinct banks; thread
+//     8*(r%16) + r/16 and a 72-dword row stride, so that the 64 lanes of a
+//     column read below address 64 different dword banks (dword address
+//     mod 64 is 8g + p mod 64) and each 16-lane row write is one contiguous
+//     256-byte row; thread
 //     (pair p, group g) then reads channels 2p, 2p+1 of tokens 16g .. 16g+15
 //     and reduces each channel over the 8 groups.
 // ---------------------------------------------------------------------------
