@@ -8,6 +8,7 @@ built, every call raises; there is no fallback.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -40,6 +41,7 @@ SIGNATURES = {
     "bf16_gemm_tn": (_INT, [_P, _P, _P, _INT, _I64, _I64, _I64, _P]),
     "fp8_encode_e4m3": (_INT, [_P, _I64, _P, _P]),
     "fp8bs_mfma_rate": (_INT, [_P, _I64, _INT, ctypes.c_float, _P]),
+    "fp8bs_hbm_rate": (_INT, [_P, _I64, _P, _P, _P]),
     "fp8bs_status_string": (ctypes.c_char_p, [_INT]),
     "fp8bs_version": (_INT, []),
 }
@@ -83,16 +85,60 @@ def _stream(t: torch.Tensor, stream):
     return None
 
 
+def _alloc_on(stream, device):
+    """Context in which torch allocates on the stream the kernels run on, so
+    that a temporary freed when the call returns (an output or an "auto"
+    workspace) is not handed to other work before the kernels are done with
+    it (the caching allocator reuses a block only on the stream it was
+    allocated on)."""
+    if stream is None:
+        return contextlib.nullcontext()
+    if not hasattr(stream, "cuda_stream"):
+        stream = torch.cuda.ExternalStream(int(stream), device=device)
+    return torch.cuda.stream(stream)
+
+
 def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
 def _need(t: torch.Tensor, dtype, shape, what):
-    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+    """t must be a contiguous tensor of `dtype` and `shape` (a None in `shape`
+    matches any size).  Checked before any call, so a mis-shaped or strided
+    tensor never reaches a kernel."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{what}: expected a tensor, got {type(t).__name__}")
+    ok_shape = t.dim() == len(shape) and all(e is None or e == d for e, d in zip(shape, t.shape))
+    if t.dtype != dtype or not ok_shape or not t.is_contiguous():
         raise ValueError(f"{what}: expected contiguous {dtype} {tuple(shape)}, "
                          f"got {t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()}")
-    if not t.is_cuda:
-        raise ValueError(f"{what}: expected a device tensor")
+
+
+def _on_device(**tensors):
+    """Every tensor given (None skipped) must live on one GPU; checked after
+    the shapes, right before the call."""
+    devs = set()
+    for what, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{what}: expected a device tensor")
+        devs.add(t.device)
+    if len(devs) > 1:
+        raise ValueError(f"tensors on different devices: {sorted(map(str, devs))}")
+
+
+def _dims(t: torch.Tensor, what):
+    if not isinstance(t, torch.Tensor) or t.dim() != 2:
+        raise ValueError(f"{what}: expected a 2-D tensor")
+    return t.shape
+
+
+def _blocks(n: int):
+    """Number of 128-wide blocks of a dimension, or None (any size accepted
+    here) when it is not a multiple of 128: the C call then rejects the shape
+    with FP8BS_ERR_SHAPE."""
+    return n // 128 if n % 128 == 0 else None
 
 
 def _bits16(x: torch.Tensor) -> torch.Tensor:
@@ -100,15 +146,21 @@ def _bits16(x: torch.Tensor) -> torch.Tensor:
 
 
 # ------------------------------------------------------------------ quantizers
+def _bf16_input(x, what):
+    M, C = _dims(x, what)
+    _need(x, torch.bfloat16, (M, C), what)
+    return M, C
+
+
 def fp8_quantize_rowtile(x: torch.Tensor, q=None, s=None, stream=None):
     """x bf16 [M,K] -> (q uint8 [M,K], s float32 [M,K/128])."""
-    M, K = x.shape
-    if x.dtype != torch.bfloat16:
-        raise ValueError("x must be bfloat16")
-    q = torch.empty((M, K), dtype=torch.uint8, device=x.device) if q is None else q
-    s = torch.empty((M, K // 128), dtype=torch.float32, device=x.device) if s is None else s
+    M, K = _bf16_input(x, "x")
+    with _alloc_on(stream, x.device):
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device) if q is None else q
+        s = torch.empty((M, K // 128), dtype=torch.float32, device=x.device) if s is None else s
     _need(q, torch.uint8, (M, K), "q")
-    _need(s, torch.float32, (M, K // 128), "s")
+    _need(s, torch.float32, (M, _blocks(K)), "s")
+    _on_device(x=x, q=q, s=s)
     _check("fp8_quantize_rowtile", capi().fp8_quantize_rowtile(
         _ptr(x), M, K, _ptr(q), _ptr(s), _stream(x, stream)))
     return q, s
@@ -117,18 +169,18 @@ def fp8_quantize_rowtile(x: torch.Tensor, q=None, s=None, stream=None):
 def fp8_quantize_block(w: torch.Tensor, q=None, q_t=None, s=None, with_transpose=True,
                        stream=None):
     """w bf16 [N,K] -> (q uint8 [N,K], q_t uint8 [K,N] or None, s float32 [N/128,K/128])."""
-    N, K = w.shape
-    if w.dtype != torch.bfloat16:
-        raise ValueError("w must be bfloat16")
+    N, K = _bf16_input(w, "w")
     dev = w.device
-    q = torch.empty((N, K), dtype=torch.uint8, device=dev) if q is None else q
-    if with_transpose and q_t is None:
-        q_t = torch.empty((K, N), dtype=torch.uint8, device=dev)
-    s = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev) if s is None else s
+    with _alloc_on(stream, dev):
+        q = torch.empty((N, K), dtype=torch.uint8, device=dev) if q is None else q
+        if with_transpose and q_t is None:
+            q_t = torch.empty((K, N), dtype=torch.uint8, device=dev)
+        s = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev) if s is None else s
     _need(q, torch.uint8, (N, K), "q")
     if q_t is not None:
         _need(q_t, torch.uint8, (K, N), "q_t")
-    _need(s, torch.float32, (N // 128, K // 128), "s")
+    _need(s, torch.float32, (_blocks(N), _blocks(K)), "s")
+    _on_device(w=w, q=q, q_t=q_t, s=s)
     _check("fp8_quantize_block", capi().fp8_quantize_block(
         _ptr(w), N, K, _ptr(q), _ptr(q_t), _ptr(s), _stream(w, stream)))
     return q, q_t, s
@@ -136,13 +188,13 @@ def fp8_quantize_block(w: torch.Tensor, q=None, q_t=None, s=None, with_transpose
 
 def fp8_quantize_transposed(x: torch.Tensor, qt=None, st=None, stream=None):
     """x bf16 [M,C] -> (qt uint8 [C,M], st float32 [C,M/128])."""
-    M, C = x.shape
-    if x.dtype != torch.bfloat16:
-        raise ValueError("x must be bfloat16")
-    qt = torch.empty((C, M), dtype=torch.uint8, device=x.device) if qt is None else qt
-    st = torch.empty((C, M // 128), dtype=torch.float32, device=x.device) if st is None else st
+    M, C = _bf16_input(x, "x")
+    with _alloc_on(stream, x.device):
+        qt = torch.empty((C, M), dtype=torch.uint8, device=x.device) if qt is None else qt
+        st = torch.empty((C, M // 128), dtype=torch.float32, device=x.device) if st is None else st
     _need(qt, torch.uint8, (C, M), "qt")
-    _need(st, torch.float32, (C, M // 128), "st")
+    _need(st, torch.float32, (C, _blocks(M)), "st")
+    _on_device(x=x, qt=qt, st=st)
     _check("fp8_quantize_transposed", capi().fp8_quantize_transposed(
         _ptr(x), M, C, _ptr(qt), _ptr(st), _stream(x, stream)))
     return qt, st
@@ -150,28 +202,29 @@ def fp8_quantize_transposed(x: torch.Tensor, qt=None, st=None, stream=None):
 
 def fp8_quantize_dual(x: torch.Tensor, q=None, s=None, qt=None, st=None, stream=None):
     """x bf16 [M,C] -> (q [M,C], s [M,C/128], qt [C,M], st [C,M/128]) in one pass."""
-    M, C = x.shape
-    if x.dtype != torch.bfloat16:
-        raise ValueError("x must be bfloat16")
+    M, C = _bf16_input(x, "x")
     dev = x.device
-    q = torch.empty((M, C), dtype=torch.uint8, device=dev) if q is None else q
-    s = torch.empty((M, C // 128), dtype=torch.float32, device=dev) if s is None else s
-    qt = torch.empty((C, M), dtype=torch.uint8, device=dev) if qt is None else qt
-    st = torch.empty((C, M // 128), dtype=torch.float32, device=dev) if st is None else st
+    with _alloc_on(stream, dev):
+        q = torch.empty((M, C), dtype=torch.uint8, device=dev) if q is None else q
+        s = torch.empty((M, C // 128), dtype=torch.float32, device=dev) if s is None else s
+        qt = torch.empty((C, M), dtype=torch.uint8, device=dev) if qt is None else qt
+        st = torch.empty((C, M // 128), dtype=torch.float32, device=dev) if st is None else st
     _need(q, torch.uint8, (M, C), "q")
-    _need(s, torch.float32, (M, C // 128), "s")
+    _need(s, torch.float32, (M, _blocks(C)), "s")
     _need(qt, torch.uint8, (C, M), "qt")
-    _need(st, torch.float32, (C, M // 128), "st")
+    _need(st, torch.float32, (C, _blocks(M)), "st")
+    _on_device(x=x, q=q, s=s, qt=qt, st=st)
     _check("fp8_quantize_dual", capi().fp8_quantize_dual(
         _ptr(x), M, C, _ptr(q), _ptr(s), _ptr(qt), _ptr(st), _stream(x, stream)))
     return q, s, qt, st
 
 
 # ----------------------------------------------------------------------- GEMMs
-def _out(shape, out_dtype, device, out):
+def _out(shape, out_dtype, device, out, stream):
     dt = torch.bfloat16 if out_dtype == FP8BS_OUT_BF16 else torch.float32
     if out is None:
-        out = torch.empty(shape, dtype=dt, device=device)
+        with _alloc_on(stream, device):
+            out = torch.empty(shape, dtype=dt, device=device)
     _need(out, dt, shape, "output")
     return out
 
@@ -184,23 +237,42 @@ def _dtype_code(out_dtype):
     raise ValueError(f"unknown output dtype {out_dtype}")
 
 
+def _row_operand(q, s, what):
+    """Codes [R, L] and scales [R, L/128] of 1x128 tiles along L."""
+    R, L = _dims(q, what)
+    _need(q, torch.uint8, (R, L), what)
+    _need(s, torch.float32, (R, _blocks(L)), what + " scales")
+    return R, L
+
+
 def fp8_gemm_fprop(xq, xs, wq, ws, out_dtype=torch.bfloat16, y=None, stream=None):
     """Y [M,N] = X W^T from (xq [M,K], xs [M,K/128]) and (wq [N,K], ws [N/128,K/128])."""
-    M, K = xq.shape
-    N = wq.shape[0]
+    M, K = _row_operand(xq, xs, "xq")
+    N, _ = _dims(wq, "wq")
+    _need(wq, torch.uint8, (N, K), "wq")
+    _need(ws, torch.float32, (_blocks(N), _blocks(K)), "ws")
     code = _dtype_code(out_dtype)
-    y = _out((M, N), code, xq.device, y)
+    y = _out((M, N), code, xq.device, y, stream)
+    _on_device(xq=xq, xs=xs, wq=wq, ws=ws, y=y)
     _check("fp8_gemm_fprop", capi().fp8_gemm_fprop(
         _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(y), code, M, N, K, _stream(xq, stream)))
     return y
 
 
+def _dgrad_operands(dyq, dys, wq_t, ws):
+    M, N = _row_operand(dyq, dys, "dyq")
+    K, _ = _dims(wq_t, "wq_t")
+    _need(wq_t, torch.uint8, (K, N), "wq_t")
+    _need(ws, torch.float32, (_blocks(N), _blocks(K)), "ws")
+    return M, N, K
+
+
 def fp8_gemm_dgrad(dyq, dys, wq_t, ws, out_dtype=torch.bfloat16, dx=None, stream=None):
     """dX [M,K] = dY W from (dyq [M,N], dys [M,N/128]) and (wq_t [K,N], ws [N/128,K/128])."""
-    M, N = dyq.shape
-    K = wq_t.shape[0]
+    M, N, K = _dgrad_operands(dyq, dys, wq_t, ws)
     code = _dtype_code(out_dtype)
-    dx = _out((M, K), code, dyq.device, dx)
+    dx = _out((M, K), code, dyq.device, dx, stream)
+    _on_device(dyq=dyq, dys=dys, wq_t=wq_t, ws=ws, dx=dx)
     _check("fp8_gemm_dgrad", capi().fp8_gemm_dgrad(
         _ptr(dyq), _ptr(dys), _ptr(wq_t), _ptr(ws), _ptr(dx), code, M, N, K, _stream(dyq, stream)))
     return dx
@@ -210,17 +282,18 @@ def fp8_gemm_dgrad_quantized(dyq, dys, wq_t, ws, with_bf16=True, dx=None, dxq=No
                              stream=None):
     """dgrad with its BF16 output quantized in 1x128 row tiles in the epilogue:
     returns (dx bf16 [M,K] or None, dxq uint8 [M,K], dxs float32 [M,K/128])."""
-    M, N = dyq.shape
-    K = wq_t.shape[0]
+    M, N, K = _dgrad_operands(dyq, dys, wq_t, ws)
     dev = dyq.device
-    if with_bf16 and dx is None:
-        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    with _alloc_on(stream, dev):
+        if with_bf16 and dx is None:
+            dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        dxq = torch.empty((M, K), dtype=torch.uint8, device=dev) if dxq is None else dxq
+        dxs = torch.empty((M, K // 128), dtype=torch.float32, device=dev) if dxs is None else dxs
     if dx is not None:
         _need(dx, torch.bfloat16, (M, K), "dx")
-    dxq = torch.empty((M, K), dtype=torch.uint8, device=dev) if dxq is None else dxq
-    dxs = torch.empty((M, K // 128), dtype=torch.float32, device=dev) if dxs is None else dxs
     _need(dxq, torch.uint8, (M, K), "dxq")
-    _need(dxs, torch.float32, (M, K // 128), "dxs")
+    _need(dxs, torch.float32, (M, _blocks(K)), "dxs")
+    _on_device(dyq=dyq, dys=dys, wq_t=wq_t, ws=ws, dx=dx, dxq=dxq, dxs=dxs)
     _check("fp8_gemm_dgrad_quantized", capi().fp8_gemm_dgrad_quantized(
         _ptr(dyq), _ptr(dys), _ptr(wq_t), _ptr(ws), _ptr(dx), _ptr(dxq), _ptr(dxs), M, N, K,
         _stream(dyq, stream)))
@@ -231,17 +304,32 @@ def fp8_gemm_wgrad_workspace_bytes(M: int, N: int, K: int) -> int:
     return int(capi().fp8_gemm_wgrad_workspace_bytes(M, N, K))
 
 
+def _wgrad_operands(dytq, dyts, xtq, xts):
+    N, M = _row_operand(dytq, dyts, "dytq")
+    K, _ = _dims(xtq, "xtq")
+    _need(xtq, torch.uint8, (K, M), "xtq")
+    _need(xts, torch.float32, (K, _blocks(M)), "xts")
+    return M, N, K
+
+
 def fp8_gemm_wgrad(dytq, dyts, xtq, xts, dw=None, workspace=None, stream=None):
     """dW [N,K] (float32) = dY^T X from (dytq [N,M], dyts [N,M/128]) and (xtq [K,M], xts [K,M/128]).
     workspace: None (no split), "auto" (allocate the queried size) or a uint8 device tensor."""
-    N, M = dytq.shape
-    K = xtq.shape[0]
-    dw = _out((N, K), FP8BS_OUT_F32, dytq.device, dw)
-    if isinstance(workspace, str) and workspace == "auto":
+    M, N, K = _wgrad_operands(dytq, dyts, xtq, xts)
+    auto = isinstance(workspace, str)
+    if auto and workspace != "auto":
+        raise ValueError(f"workspace: expected None, 'auto' or a tensor, got {workspace!r}")
+    if not auto and workspace is not None:
+        _need(workspace, torch.uint8, (None,), "workspace")
+    _on_device(dytq=dytq, dyts=dyts, xtq=xtq, xts=xts)
+    dw = _out((N, K), FP8BS_OUT_F32, dytq.device, dw, stream)
+    if auto:
         nbytes = fp8_gemm_wgrad_workspace_bytes(M, N, K)
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dytq.device) if nbytes else None
+        with _alloc_on(stream, dytq.device):
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=dytq.device) if nbytes else None
     ws_ptr = _ptr(workspace)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    _on_device(dytq=dytq, dyts=dyts, xtq=xtq, xts=xts, dw=dw, workspace=workspace)
     _check("fp8_gemm_wgrad", capi().fp8_gemm_wgrad(
         _ptr(dytq), _ptr(dyts), _ptr(xtq), _ptr(xts), _ptr(dw), M, N, K, ws_ptr, ws_bytes,
         _stream(dytq, stream)))
@@ -250,14 +338,12 @@ def fp8_gemm_wgrad(dytq, dyts, xtq, xts, dw=None, workspace=None, stream=None):
 
 def bf16_gemm_tn(a: torch.Tensor, b: torch.Tensor, out_dtype=torch.bfloat16, c=None, stream=None):
     """C [I,J] = A B^T for BF16 A [I,K], B [J,K] (the unquantized comparator)."""
-    if a.dtype != torch.bfloat16 or b.dtype != torch.bfloat16:
-        raise ValueError("a and b must be bfloat16")
-    I, K = a.shape
-    J = b.shape[0]
-    if b.shape[1] != K:
-        raise ValueError("contraction lengths differ")
+    I, K = _bf16_input(a, "a")
+    J, _ = _dims(b, "b")
+    _need(b, torch.bfloat16, (J, K), "b")
     code = _dtype_code(out_dtype)
-    c = _out((I, J), code, a.device, c)
+    c = _out((I, J), code, a.device, c, stream)
+    _on_device(a=a, b=b, c=c)
     _check("bf16_gemm_tn", capi().bf16_gemm_tn(_bits16(a).data_ptr(), _bits16(b).data_ptr(),
                                                _ptr(c), code, I, J, K, _stream(a, stream)))
     return c
@@ -265,8 +351,14 @@ def bf16_gemm_tn(a: torch.Tensor, b: torch.Tensor, out_dtype=torch.bfloat16, c=N
 
 def fp8_encode_e4m3(x: torch.Tensor, q=None, stream=None):
     """Diagnostic: x float32 [n] -> E4M3 codes of clamp(x, -448, 448)."""
+    if not isinstance(x, torch.Tensor):
+        raise ValueError("x: expected a tensor")
     x = x.reshape(-1)
-    q = torch.empty(x.numel(), dtype=torch.uint8, device=x.device) if q is None else q
+    _need(x, torch.float32, (x.numel(),), "x")
+    with _alloc_on(stream, x.device):
+        q = torch.empty(x.numel(), dtype=torch.uint8, device=x.device) if q is None else q
+    _need(q, torch.uint8, (x.numel(),), "q")
+    _on_device(x=x, q=q)
     _check("fp8_encode_e4m3", capi().fp8_encode_e4m3(_ptr(x), x.numel(), _ptr(q),
                                                      _stream(x, stream)))
     return q
@@ -277,10 +369,37 @@ def fp8bs_mfma_rate(blocks: int, iters: int, v: float = 0.125, out=None, device=
     """Diagnostic: MFMA-only work of blocks x 256 threads (blocks * 4 * iters *
     128 * 16384 flop); returns the float32 [blocks * 256] results, each
     16384 * v^2 * iters."""
-    out = torch.empty(blocks * 256, dtype=torch.float32, device=device) if out is None else out
+    if out is None:
+        with _alloc_on(stream, device):
+            out = torch.empty(blocks * 256, dtype=torch.float32, device=device)
+    _need(out, torch.float32, (blocks * 256,), "out")
+    _on_device(out=out)
     _check("fp8bs_mfma_rate", capi().fp8bs_mfma_rate(_ptr(out), blocks, iters, v,
                                                      _stream(out, stream)))
     return out
+
+
+def fp8bs_hbm_rate(x: torch.Tensor, y0=None, y1=None, two_outputs=False, stream=None):
+    """Diagnostic: the quantizers' streaming traffic (2 bytes read, 1 or 2
+    written per element) without their arithmetic.  x is viewed as n BF16
+    bit patterns; returns (y0, y1): the high bytes and (two_outputs) the low
+    bytes of x, uint8 [n]."""
+    if not isinstance(x, torch.Tensor) or x.dtype not in (torch.bfloat16, torch.int16):
+        raise ValueError("x: expected a bfloat16 or int16 tensor")
+    x = x.reshape(-1)
+    _need(x, x.dtype, (x.numel(),), "x")
+    n = x.numel()
+    with _alloc_on(stream, x.device):
+        y0 = torch.empty(n, dtype=torch.uint8, device=x.device) if y0 is None else y0
+        if two_outputs and y1 is None:
+            y1 = torch.empty(n, dtype=torch.uint8, device=x.device)
+    _need(y0, torch.uint8, (n,), "y0")
+    if y1 is not None:
+        _need(y1, torch.uint8, (n,), "y1")
+    _on_device(x=x, y0=y0, y1=y1)
+    _check("fp8bs_hbm_rate", capi().fp8bs_hbm_rate(_ptr(x), n, _ptr(y0), _ptr(y1),
+                                                   _stream(x, stream)))
+    return y0, y1
 
 
 def fp8bs_status_string(status: int) -> str:

@@ -3,7 +3,8 @@
 // Each entry point validates its arguments completely before anything is
 // enqueued, then calls one launcher on the caller's stream.  The only state
 // kept is a per-device record of whether the device is gfx950 and how many
-// compute units it has, filled on the first call that reaches a device.
+// compute units it has, filled by the first call on a device whose
+// properties query succeeds.
 #include "../../include/fp8bs.h"
 
 #include <hip/hip_runtime.h>
@@ -19,25 +20,34 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 
+// Per device: 0 = not yet known, 1 = gfx950, 2 = another device.  Written
+// once the properties query has succeeded; a failed query is reported as
+// FP8BS_ERR_HIP and asked again on the next call.
 struct DeviceInfo {
-    std::once_flag once;
-    bool supported = false;
-    int num_cus = 0;
+    std::atomic<int> state{0};
+    std::atomic<int> num_cus{0};
 };
 DeviceInfo g_devices[kMaxDevices];
+std::mutex g_device_mutex;
 
 fp8bs_status check_device(int* num_cus) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP8BS_ERR_HIP;
     DeviceInfo& d = g_devices[dev];
-    std::call_once(d.once, [&] {
-        hipDeviceProp_t prop;
-        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return;
-        d.supported = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-        d.num_cus = prop.multiProcessorCount;
-    });
-    if (!d.supported) return FP8BS_ERR_UNSUPPORTED;
-    *num_cus = d.num_cus;
+    int state = d.state.load(std::memory_order_acquire);
+    if (state == 0) {
+        std::lock_guard<std::mutex> lock(g_device_mutex);
+        state = d.state.load(std::memory_order_acquire);
+        if (state == 0) {
+            hipDeviceProp_t prop;
+            if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FP8BS_ERR_HIP;
+            d.num_cus.store(prop.multiProcessorCount, std::memory_order_relaxed);
+            state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+            d.state.store(state, std::memory_order_release);
+        }
+    }
+    if (state != 1) return FP8BS_ERR_UNSUPPORTED;
+    *num_cus = d.num_cus.load(std::memory_order_relaxed);
     return FP8BS_OK;
 }
 
@@ -235,6 +245,18 @@ fp8bs_status fp8_encode_e4m3(const float* x, int64_t n, uint8_t* q, fp8bs_stream
     int cus;
     FP8BS_TRY(check_device(&cus));
     return launched(fp8bs::launch_encode_e4m3(x, n, q, stream));
+}
+
+fp8bs_status fp8bs_hbm_rate(const uint16_t* x, int64_t n, uint8_t* y0, uint8_t* y1,
+                            fp8bs_stream_t stream) {
+    if (n < 0) return FP8BS_ERR_SHAPE;
+    FP8BS_TRY(check_ptr(x, n == 0, 16));
+    FP8BS_TRY(check_ptr(y0, n == 0, 16));
+    if (y1 && !aligned(y1, 16)) return FP8BS_ERR_ALIGN;
+    if (n == 0) return FP8BS_OK;
+    int cus;
+    FP8BS_TRY(check_device(&cus));
+    return launched(fp8bs::launch_hbm_rate(x, n, y0, y1, stream));
 }
 
 fp8bs_status fp8bs_mfma_rate(float* out, int64_t blocks, int iters, float v,

@@ -39,9 +39,16 @@
 // (gemm_common.h).  The MFMA operands are swapped (B fragment as the first
 // source) so that each lane owns four consecutive output columns of one row
 // and stores them as one vector.
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
+#include <functional>
+#include <map>
+#include <mutex>
+#include <queue>
+#include <tuple>
 #include <type_traits>
+#include <vector>
 
 #include "device_common.h"
 #include "gemm_common.h"
@@ -61,6 +68,21 @@ __device__ __forceinline__ v8h widen8(uint32_t lo, uint32_t hi) {
     return v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// Contraction split of a FP32-output GEMM: piece 0 sums blocks [0, p0) and
+// writes the output itself; piece y >= 1 sums blocks [p0 + (y-1) nps,
+// p0 + y nps) (the last one clipped to the contraction) into FP32 slice y-1
+// of the workspace Wsp.  splitk_reduce_kernel then adds the slices to the
+// output in piece order.  An unsplit launch has p0 = the block count.
+__device__ __forceinline__ int split_begin(int y, int p0, int nps) {
+    return y == 0 ? 0 : p0 + (y - 1) * nps;
+}
+__device__ __forceinline__ int split_end(int y, int p0, int nps, int nkb_all) {
+    return min(nkb_all, y == 0 ? p0 : p0 + y * nps);
+}
+__device__ __forceinline__ float* split_out(int y, void* C, float* Wsp, int64_t I, int64_t J) {
+    return y == 0 ? reinterpret_cast<float*>(C) : Wsp + (int64_t)(y - 1) * I * J;
+}
+
 constexpr int kBM = 128;
 constexpr int kBN = 128;
 constexpr int kBK = 128;
@@ -71,7 +93,7 @@ template <int MODE, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads, 2) void gemm_bs_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
     const float* __restrict__ sB, void* __restrict__ C, int64_t I, int64_t J, int64_t Kc,
-    int tiles_i, int tiles_j, int nps) {
+    int tiles_i, int tiles_j, int p0, int nps, float* __restrict__ Wsp) {
     __shared__ __align__(16) uint8_t As[2][kTileBytes];
     __shared__ __align__(16) uint8_t Bs[2][kTileBytes];
     __shared__ __align__(16) float sAs[2][kBM];
@@ -85,8 +107,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bs_fp8_kernel(
     tile_coords(blockIdx.x, tiles_i, tiles_j, &ti, &tj);
     const int64_t i0 = (int64_t)ti * kBM, j0 = (int64_t)tj * kBN;
     const int nkb_all = (int)(Kc / kBK);
-    const int kb0 = blockIdx.y * nps;                 // split s: blocks [s*nps, (s+1)*nps)
-    const int nkb = min(nkb_all, kb0 + nps) - kb0;
+    const int kb0 = split_begin(blockIdx.y, p0, nps);
+    const int nkb = split_end(blockIdx.y, p0, nps, nkb_all) - kb0;
     const int64_t jb_count = J / kBN;
 
     // Direct global -> LDS loads: wave w fills 1 KB pieces 4w .. 4w+3 of each
@@ -229,7 +251,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bs_fp8_kernel(
                 pk.y = pack_bf16x2(acc[it][jt][2], acc[it][jt][3]);
                 *reinterpret_cast<uint2*>(Cb + i * J + j) = pk;
             } else {
-                float* Cf = reinterpret_cast<float*>(C) + (int64_t)blockIdx.y * I * J;
+                float* Cf = split_out(blockIdx.y, C, Wsp, I, J);
                 *reinterpret_cast<float4*>(Cf + i * J + j) =
                     make_float4(acc[it][jt][0], acc[it][jt][1], acc[it][jt][2], acc[it][jt][3]);
             }
@@ -268,8 +290,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bs_fp8_kernel(
 // (r16, g) supplies codes [32g + 8c, 32g + 8c + 8) of its row to MFMA chunk c,
 // so one 32-byte global load per row gives a lane its four chunks.
 // Tiles are ordered for the L2s (tile_coords); gridDim.y splits the
-// contraction: split s sums blocks [s*nps, (s+1)*nps) into its own FP32 slice
-// of C.
+// contraction (split_begin / split_end / split_out).
 // QOUT: the epilogue also quantizes the BF16 output in 1x128 row tiles (the
 // rule of quant_rowtile_kernel) and stores codes Cq [I, J] and scales
 // Cs [I, J/128]; C (BF16) may then be null.  A wave's 256 output columns of a
@@ -288,8 +309,8 @@ template <int MODE, bool OUT_BF16, bool QOUT = false>
 __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
     const float* __restrict__ sB, void* __restrict__ C, int64_t I, int64_t J, int64_t Kc,
-    int tiles_i, int tiles_j, int nps, uint8_t* __restrict__ Cq = nullptr,
-    float* __restrict__ Cs = nullptr) {
+    int tiles_i, int tiles_j, int p0, int nps, float* __restrict__ Wsp,
+    uint8_t* __restrict__ Cq, float* __restrict__ Cs) {
     __shared__ __align__(16) uint8_t Bh[2][kF16Tile];
     __shared__ __align__(16) float sBs[2][MODE == kScaleRow ? kBigN : 4];   // per-row B scales
 
@@ -302,8 +323,8 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
     tile_coords(blockIdx.x, tiles_i, tiles_j, &ti, &tj);
     const int64_t i0 = (int64_t)ti * kBigM, j0 = (int64_t)tj * kBigN;
     const int nkb_all = (int)(Kc / kBK);
-    const int kb0 = blockIdx.y * nps;
-    const int nkb = min(nkb_all, kb0 + nps) - kb0;
+    const int kb0 = split_begin(blockIdx.y, p0, nps);
+    const int nkb = split_end(blockIdx.y, p0, nps, nkb_all) - kb0;
     const int64_t jb_count = J / kBN;
 
     // A: rows 32w + 16it + r16 (clamped; rows past I are never stored), the
@@ -479,7 +500,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
         } else if constexpr (OUT_BF16) {
             store_bf16(reinterpret_cast<uint16_t*>(C));
         } else {
-            float* Cf = reinterpret_cast<float*>(C) + (int64_t)blockIdx.y * I * J;
+            float* Cf = split_out(blockIdx.y, C, Wsp, I, J);
 #pragma unroll
             for (int it = 0; it < 2; ++it) {
                 const int64_t i = i0 + 32 * wave + 16 * it + r16;
@@ -615,15 +636,16 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
     out_half(std::integral_constant<int, 1>{}, lbuf);
 }
 
-// Sum of the split slices, in split order: out[e] = sum_s ws[s][e] (fixed order,
-// so the result does not depend on timing).
+// Sum of the split pieces, in piece order: out[e] = (((out[e] + ws[0][e]) +
+// ws[1][e]) + ...), where out already holds piece 0 (fixed order, so the
+// result does not depend on timing).
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float4* __restrict__ ws,
                                                             float4* __restrict__ out, int64_t n4,
-                                                            int splits) {
+                                                            int slices) {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (e >= n4) return;
-    float4 a = ws[e];
-    for (int s = 1; s < splits; ++s) {
+    float4 a = out[e];
+    for (int s = 0; s < slices; ++s) {
         const float4 b = ws[(int64_t)s * n4 + e];
         a.x += b.x;
         a.y += b.y;
@@ -635,35 +657,35 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float4* __rest
 
 template <int MODE, bool BF16>
 static hipError_t launch_small(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB,
-                               void* C, int64_t I, int64_t J, int64_t Kc, int splits, int nps,
-                               hipStream_t stream) {
+                               void* C, int64_t I, int64_t J, int64_t Kc, int pieces, int p0,
+                               int nps, float* Wsp, hipStream_t stream) {
     int64_t tiles_i = (I + kBM - 1) / kBM;
     int64_t tiles_j = J / kBN;
     int64_t blocks = tiles_i * tiles_j;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((gemm_bs_fp8_kernel<MODE, BF16>), dim3((unsigned)blocks, splits),
-                       dim3(kThreads), 0, stream, A, sA, B, sB, C, I, J, Kc, (int)tiles_i,
-                       (int)tiles_j, nps);
-    return hipGetLastError();
+    return launch(gemm_bs_fp8_kernel<MODE, BF16>, dim3((unsigned)blocks, pieces), dim3(kThreads),
+                  stream, A, sA, B, sB, C, I, J, Kc, (int)tiles_i, (int)tiles_j, p0, nps, Wsp);
 }
 
 template <int MODE, bool BF16>
 static hipError_t launch_big(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB,
-                             void* C, int64_t I, int64_t J, int64_t Kc, int splits, int nps,
-                             hipStream_t stream) {
+                             void* C, int64_t I, int64_t J, int64_t Kc, int pieces, int p0,
+                             int nps, float* Wsp, hipStream_t stream) {
     int tiles_i = (int)((I + kBigM - 1) / kBigM);
     int tiles_j = (int)((J + kBigN - 1) / kBigN);
-    hipLaunchKernelGGL((gemm_bs_fp8_big_kernel<MODE, BF16>), dim3(tiles_i * tiles_j, splits),
-                       dim3(kBigThreads), 0, stream, A, sA, B, sB, C, I, J, Kc, tiles_i, tiles_j,
-                       nps);
-    return hipGetLastError();
+    return launch(gemm_bs_fp8_big_kernel<MODE, BF16>, dim3(tiles_i * tiles_j, pieces),
+                  dim3(kBigThreads), stream, A, sA, B, sB, C, I, J, Kc, tiles_i, tiles_j, p0, nps,
+                  Wsp, (uint8_t*)nullptr, (float*)nullptr);
 }
 
-// Launch plan for one GEMM: which kernel, and how many contraction splits.
+// Launch plan for one GEMM: which kernel, and how its contraction is split
+// (split_begin / split_end: piece 0 has p0 blocks, the others nps, the last
+// clipped).
 struct Plan {
     bool big;
-    int splits;
-    int nps;     // contraction blocks per split
+    int pieces;    // 1: no split
+    int p0;
+    int nps;
 };
 
 // FP8BS_GEMM_KERNEL=small|big forces one kernel (a testing aid; the default
@@ -677,12 +699,36 @@ static int kernel_override() {
     return 0;
 }
 
-static Plan plan_gemm(ScaleMode mode, int64_t I, int64_t J, int64_t Kc, int num_cus,
-                      bool allow_split) {
-    Plan p{false, 1, (int)(Kc / kBK)};
+// Time at which the last workgroup of a split launch finishes, in units of
+// one contraction block: the dispatcher hands workgroups out in launch order
+// (every tile's piece 0, then every tile's piece 1, ...) to the first of
+// `slots` resident places to come free, and a workgroup takes its block
+// count plus a fixed per-workgroup cost (prologue, first loads, epilogue),
+// taken here as three blocks.
+static int64_t split_makespan(int64_t tiles, int64_t slots, int64_t nkb, int pieces, int p0,
+                              int nps) {
+    constexpr int64_t kFixed = 3;
+    std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
+    for (int64_t i = 0; i < slots; ++i) free_at.push(0);
+    int64_t end = 0;
+    for (int y = 0; y < pieces; ++y) {
+        const int64_t b0 = y == 0 ? 0 : p0 + (int64_t)(y - 1) * nps;
+        const int64_t b1 = std::min<int64_t>(nkb, y == 0 ? p0 : p0 + (int64_t)y * nps);
+        const int64_t len = b1 - b0 + kFixed;
+        for (int64_t t = 0; t < tiles; ++t) {
+            const int64_t start = free_at.top();
+            free_at.pop();
+            free_at.push(start + len);
+            end = std::max(end, start + len);
+        }
+    }
+    return end;
+}
+
+static Plan plan_gemm_uncached(ScaleMode mode, int64_t I, int64_t J, int64_t Kc, int cus,
+                               bool allow_split, int force) {
     const int64_t nkb = Kc / kBK;
-    const int cus = num_cus > 0 ? num_cus : 256;
-    const int force = kernel_override();
+    Plan p{false, 1, (int)nkb, (int)nkb};
     if (nkb == 0) return p;
     const int64_t big_tiles = ((I + kBigM - 1) / kBigM) * ((J + kBigN - 1) / kBigN);
     const int64_t small_tiles = ((I + kBM - 1) / kBM) * (J / kBN);
@@ -694,34 +740,60 @@ static Plan plan_gemm(ScaleMode mode, int64_t I, int64_t J, int64_t Kc, int num_
     else if (force == 1) p.big = false;
     else p.big = I >= kBigM && (mode == kScaleRow ? (allow_split || big_tiles < cus)
                                                    : big_tiles >= cus);
-    // Split the contraction (FP32 output only, with a caller workspace) into
-    // s = 1, 2, 4, ... parts, taking the s that minimizes (full waves of
-    // resident workgroups) x (contraction blocks per workgroup); ties go to
-    // the smaller s, whose reduction pass is cheaper.
-    if (mode == kScaleRow && allow_split) {
-        const int64_t tiles = p.big ? big_tiles : small_tiles;
-        const int64_t slots = p.big ? cus : 2 * cus;           // workgroups resident at once
-        int best = 1;
-        int64_t best_cost = -1;
-        for (int s = 1; s <= 16 && nkb / s >= 4; s *= 2) {
-            const int64_t cost = ((tiles * s + slots - 1) / slots) * ((nkb + s - 1) / s);
-            if (best_cost < 0 || cost < best_cost) {
-                best_cost = cost;
-                best = s;
-            }
+    if (mode != kScaleRow || !allow_split) return p;
+    // Split the contraction (FP32 output with a caller workspace) when that
+    // shortens the launch: candidates are equal pieces (2 .. 8 of them, at
+    // least 4 blocks each) and two unequal pieces, the longer first; the one
+    // with the earliest simulated finish wins, ties going to fewer pieces
+    // (each piece after the first costs an FP32 slice written and read back).
+    const int64_t tiles = p.big ? big_tiles : small_tiles;
+    const int64_t slots = p.big ? cus : 2 * (int64_t)cus;     // workgroups resident at once
+    if (tiles >= 4 * slots || tiles * 8 > (int64_t)1 << 20) return p;
+    int64_t best = split_makespan(tiles, slots, nkb, 1, (int)nkb, (int)nkb);
+    auto consider = [&](int pieces, int p0, int nps) {
+        const int64_t t = split_makespan(tiles, slots, nkb, pieces, p0, nps);
+        if (t < best || (t == best && pieces < p.pieces)) {
+            best = t;
+            p.pieces = pieces;
+            p.p0 = p0;
+            p.nps = nps;
         }
-        if (best > 1) {
-            p.nps = (int)((nkb + best - 1) / best);
-            p.splits = (int)((nkb + p.nps - 1) / p.nps);
-        }
+    };
+    for (int s = 2; s <= 8 && nkb / s >= 4; ++s) {
+        const int nps = (int)((nkb + s - 1) / s);
+        consider((int)((nkb - nps + nps - 1) / nps) + 1, nps, nps);
     }
+    const int step = (int)std::max<int64_t>(1, nkb / 32);
+    for (int64_t p0 = (nkb + 1) / 2 + step; p0 <= nkb - 4; p0 += step)
+        consider(2, (int)p0, (int)(nkb - p0));
+    return p;
+}
+
+// Plans depend only on the shape, the device's CU count and the options, so
+// each is simulated once per process.
+static Plan plan_gemm(ScaleMode mode, int64_t I, int64_t J, int64_t Kc, int num_cus,
+                      bool allow_split) {
+    const int cus = num_cus > 0 ? num_cus : 256;
+    const int force = kernel_override();
+    static std::mutex mu;
+    static std::map<std::tuple<int, int64_t, int64_t, int64_t, int, bool, int>, Plan> cache;
+    const auto key = std::make_tuple((int)mode, I, J, Kc, cus, allow_split, force);
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        auto it = cache.find(key);
+        if (it != cache.end()) return it->second;
+    }
+    const Plan p = plan_gemm_uncached(mode, I, J, Kc, cus, allow_split, force);
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache.size() > 4096) cache.clear();
+    cache.emplace(key, p);
     return p;
 }
 
 size_t gemm_workspace_bytes(ScaleMode mode, int64_t I, int64_t J, int64_t Kc, int num_cus) {
     Plan p = plan_gemm(mode, I, J, Kc, num_cus, true);
-    if (p.splits <= 1) return 0;
-    return (size_t)p.splits * (size_t)I * (size_t)J * sizeof(float);
+    if (p.pieces <= 1) return 0;
+    return (size_t)(p.pieces - 1) * (size_t)I * (size_t)J * sizeof(float);
 }
 
 template <int MODE>
@@ -732,23 +804,22 @@ static hipError_t launch_mode(const uint8_t* A, const float* sA, const uint8_t* 
     const size_t need = gemm_workspace_bytes((ScaleMode)MODE, I, J, Kc, num_cus);
     const bool can_split = !out_bf16 && workspace && need > 0 && workspace_bytes >= need;
     Plan p = plan_gemm((ScaleMode)MODE, I, J, Kc, num_cus, can_split);
-    if (p.splits <= 1) {
-        if (p.big)
-            return out_bf16 ? launch_big<MODE, true>(A, sA, B, sB, C, I, J, Kc, 1, p.nps, stream)
-                            : launch_big<MODE, false>(A, sA, B, sB, C, I, J, Kc, 1, p.nps, stream);
-        return out_bf16 ? launch_small<MODE, true>(A, sA, B, sB, C, I, J, Kc, 1, p.nps, stream)
-                        : launch_small<MODE, false>(A, sA, B, sB, C, I, J, Kc, 1, p.nps, stream);
-    }
-    hipError_t e = p.big ? launch_big<MODE, false>(A, sA, B, sB, workspace, I, J, Kc, p.splits,
-                                                   p.nps, stream)
-                         : launch_small<MODE, false>(A, sA, B, sB, workspace, I, J, Kc, p.splits,
-                                                     p.nps, stream);
-    if (e != hipSuccess) return e;
+    float* Wsp = p.pieces > 1 ? reinterpret_cast<float*>(workspace) : nullptr;
+    hipError_t e;
+    if (out_bf16)
+        e = p.big ? launch_big<MODE, true>(A, sA, B, sB, C, I, J, Kc, 1, p.p0, p.nps, nullptr, stream)
+                  : launch_small<MODE, true>(A, sA, B, sB, C, I, J, Kc, 1, p.p0, p.nps, nullptr,
+                                             stream);
+    else
+        e = p.big ? launch_big<MODE, false>(A, sA, B, sB, C, I, J, Kc, p.pieces, p.p0, p.nps, Wsp,
+                                            stream)
+                  : launch_small<MODE, false>(A, sA, B, sB, C, I, J, Kc, p.pieces, p.p0, p.nps,
+                                              Wsp, stream);
+    if (e != hipSuccess || p.pieces <= 1) return e;
     const int64_t n4 = I * J / 4;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0,
-                       stream, reinterpret_cast<const float4*>(workspace),
-                       reinterpret_cast<float4*>(C), n4, p.splits);
-    return hipGetLastError();
+    return launch(splitk_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), stream,
+                  reinterpret_cast<const float4*>(Wsp), reinterpret_cast<float4*>(C), n4,
+                  p.pieces - 1);
 }
 
 hipError_t launch_gemm_quantized(ScaleMode mode, const uint8_t* A, const float* sA,
@@ -759,16 +830,14 @@ hipError_t launch_gemm_quantized(ScaleMode mode, const uint8_t* A, const float* 
     const int nkb = (int)(Kc / kBK);
     if (tiles_i == 0 || tiles_j == 0) return hipSuccess;
     if (mode == kScaleBlockT)
-        hipLaunchKernelGGL((gemm_bs_fp8_big_kernel<kScaleBlockT, true, true>),
-                           dim3(tiles_i * tiles_j, 1), dim3(kBigThreads), 0, stream, A, sA, B, sB,
-                           (void*)C, I, J, Kc, tiles_i, tiles_j, nkb, Cq, Cs);
-    else if (mode == kScaleBlock)
-        hipLaunchKernelGGL((gemm_bs_fp8_big_kernel<kScaleBlock, true, true>),
-                           dim3(tiles_i * tiles_j, 1), dim3(kBigThreads), 0, stream, A, sA, B, sB,
-                           (void*)C, I, J, Kc, tiles_i, tiles_j, nkb, Cq, Cs);
-    else
-        return hipErrorInvalidValue;
-    return hipGetLastError();
+        return launch(gemm_bs_fp8_big_kernel<kScaleBlockT, true, true>, dim3(tiles_i * tiles_j, 1),
+                      dim3(kBigThreads), stream, A, sA, B, sB, (void*)C, I, J, Kc, tiles_i,
+                      tiles_j, nkb, nkb, (float*)nullptr, Cq, Cs);
+    if (mode == kScaleBlock)
+        return launch(gemm_bs_fp8_big_kernel<kScaleBlock, true, true>, dim3(tiles_i * tiles_j, 1),
+                      dim3(kBigThreads), stream, A, sA, B, sB, (void*)C, I, J, Kc, tiles_i,
+                      tiles_j, nkb, nkb, (float*)nullptr, Cq, Cs);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm(ScaleMode mode, const uint8_t* A, const float* sA, const uint8_t* B,
@@ -818,8 +887,7 @@ __global__ __launch_bounds__(256) void mfma_rate_kernel(float* __restrict__ out,
 
 hipError_t launch_mfma_rate(float* out, int64_t blocks, int iters, float v, hipStream_t stream) {
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(mfma_rate_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, out, iters, v);
-    return hipGetLastError();
+    return launch(mfma_rate_kernel, dim3((unsigned)blocks), dim3(256), stream, out, iters, v);
 }
 
 }  // namespace fp8bs

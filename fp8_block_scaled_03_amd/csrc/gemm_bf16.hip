@@ -174,12 +174,10 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* B, void* C, bool 
     const int64_t blocks = tiles_i * tiles_j;
     if (blocks == 0) return hipSuccess;
     if (out_bf16)
-        hipLaunchKernelGGL(gemm_bf16_kernel<true>, dim3((unsigned)blocks), dim3(kB16Threads), 0,
-                           stream, A, B, C, I, J, K, (int)tiles_i, (int)tiles_j);
-    else
-        hipLaunchKernelGGL(gemm_bf16_kernel<false>, dim3((unsigned)blocks), dim3(kB16Threads), 0,
-                           stream, A, B, C, I, J, K, (int)tiles_i, (int)tiles_j);
-    return hipGetLastError();
+        return launch(gemm_bf16_kernel<true>, dim3((unsigned)blocks), dim3(kB16Threads), stream, A,
+                      B, C, I, J, K, (int)tiles_i, (int)tiles_j);
+    return launch(gemm_bf16_kernel<false>, dim3((unsigned)blocks), dim3(kB16Threads), stream, A, B,
+                  C, I, J, K, (int)tiles_i, (int)tiles_j);
 }
 
 }  // namespace fp8bs

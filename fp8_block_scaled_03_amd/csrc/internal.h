@@ -5,7 +5,27 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <tuple>
+
 namespace fp8bs {
+
+// Launch kernel k on stream with the given arguments (converted to the
+// kernel's parameter types) and return the status of this launch alone:
+// hipLaunchKernel reports its own failure directly, so an error left behind
+// by an earlier, unrelated HIP call on this thread is never returned (nor
+// cleared) here.
+template <typename... KArgs, typename... Args>
+inline hipError_t launch(void (*k)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+                         Args... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
+    std::tuple<KArgs...> values(args...);
+    return std::apply(
+        [&](auto&... v) {
+            void* ptrs[] = {static_cast<void*>(&v)...};
+            return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, ptrs, 0, stream);
+        },
+        values);
+}
 
 // How the B operand's scale for (row j, contraction block kb) is found.
 enum ScaleMode : int {
@@ -43,6 +63,10 @@ hipError_t launch_gemm_quantized(ScaleMode mode, const uint8_t* A, const float* 
 // C[I, J] = A B^T with A [I, K], B [J, K] BF16 (unquantized comparator).
 hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* B, void* C, bool out_bf16,
                             int64_t I, int64_t J, int64_t K, hipStream_t stream);
+
+// Diagnostic: y0[i] = high byte of x[i], y1[i] (if y1) = low byte (hbm_rate_kernel).
+hipError_t launch_hbm_rate(const uint16_t* x, int64_t n, uint8_t* y0, uint8_t* y1,
+                           hipStream_t stream);
 
 // Diagnostic: blocks x 256 threads of MFMA-only work (see mfma_rate_kernel).
 hipError_t launch_mfma_rate(float* out, int64_t blocks, int iters, float v, hipStream_t stream);

@@ -67,9 +67,8 @@ hipError_t launch_quant_rowtile(const uint16_t* x, int64_t M, int64_t K, uint8_t
     int64_t ntiles = M * (K / kTile);
     if (ntiles == 0) return hipSuccess;
     int64_t blocks = (ntiles + kRowTilesPerBlock - 1) / kRowTilesPerBlock;
-    hipLaunchKernelGGL(quant_rowtile_kernel, dim3((unsigned)blocks), dim3(kRowThreads), 0, stream,
-                       reinterpret_cast<const uint4*>(x), reinterpret_cast<uint2*>(q), s, ntiles);
-    return hipGetLastError();
+    return launch(quant_rowtile_kernel, dim3((unsigned)blocks), dim3(kRowThreads), stream,
+                  reinterpret_cast<const uint4*>(x), reinterpret_cast<uint2*>(q), s, ntiles);
 }
 
 // ---------------------------------------------------------------------------
@@ -157,9 +156,8 @@ hipError_t launch_quant_block(const uint16_t* w, int64_t N, int64_t K, uint8_t* 
                               float* s, hipStream_t stream) {
     int64_t blocks = (N / kTile) * (K / kTile);
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(quant_block_kernel, dim3((unsigned)blocks), dim3(kBlkThreads), 0, stream, w,
-                       N, K, q, q_t, s);
-    return hipGetLastError();
+    return launch(quant_block_kernel, dim3((unsigned)blocks), dim3(kBlkThreads), stream, w, N, K,
+                  q, q_t, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -272,18 +270,16 @@ hipError_t launch_quant_transposed(const uint16_t* x, int64_t M, int64_t C, uint
                                    hipStream_t stream) {
     int64_t blocks = (M / kTile) * (C / kTile);
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(quant_dual_kernel<false>, dim3((unsigned)blocks), dim3(kDualThreads), 0,
-                       stream, x, M, C, (uint8_t*)nullptr, (float*)nullptr, qt, st);
-    return hipGetLastError();
+    return launch(quant_dual_kernel<false>, dim3((unsigned)blocks), dim3(kDualThreads), stream, x,
+                  M, C, (uint8_t*)nullptr, (float*)nullptr, qt, st);
 }
 
 hipError_t launch_quant_dual(const uint16_t* x, int64_t M, int64_t C, uint8_t* q, float* s,
                              uint8_t* qt, float* st, hipStream_t stream) {
     int64_t blocks = (M / kTile) * (C / kTile);
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(quant_dual_kernel<true>, dim3((unsigned)blocks), dim3(kDualThreads), 0, stream,
-                       x, M, C, q, s, qt, st);
-    return hipGetLastError();
+    return launch(quant_dual_kernel<true>, dim3((unsigned)blocks), dim3(kDualThreads), stream, x, M,
+                  C, q, s, qt, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -305,8 +301,45 @@ __global__ __launch_bounds__(256) void encode_e4m3_kernel(const float* __restric
 hipError_t launch_encode_e4m3(const float* x, int64_t n, uint8_t* q, hipStream_t stream) {
     if (n == 0) return hipSuccess;
     int64_t blocks = (n + 1023) / 1024;
-    hipLaunchKernelGGL(encode_e4m3_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, n, q);
-    return hipGetLastError();
+    return launch(encode_e4m3_kernel, dim3((unsigned)blocks), dim3(256), stream, x, n, q);
+}
+
+// ---------------------------------------------------------------------------
+// Diagnostic: the quantizers' memory traffic without their arithmetic.  Each
+// thread reads 16 BF16 values (32 bytes, non-temporal) and writes their 16
+// high bytes to y0 and, when y1 is given, their 16 low bytes to y1: 2 bytes
+// read and 1 or 2 bytes written per element, in 16-byte accesses, the
+// streaming pattern of the row-tile / token-axis quantizers (one code array)
+// and of the dual-axis quantizer (two).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void hbm_rate_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                       uint8_t* __restrict__ y0,
+                                                       uint8_t* __restrict__ y1) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 16;
+    if (i + 16 <= n) {
+        const uint4 a = load_stream16(x + i);
+        const uint4 b = load_stream16(x + i + 8);
+        // bytes 1, 3, 5, 7 of each 8-byte half: the high bytes of four values
+        auto hi4 = [](uint32_t u, uint32_t v) { return __builtin_amdgcn_perm(v, u, 0x07050301u); };
+        auto lo4 = [](uint32_t u, uint32_t v) { return __builtin_amdgcn_perm(v, u, 0x06040200u); };
+        *reinterpret_cast<uint4*>(y0 + i) =
+            make_uint4(hi4(a.x, a.y), hi4(a.z, a.w), hi4(b.x, b.y), hi4(b.z, b.w));
+        if (y1)
+            *reinterpret_cast<uint4*>(y1 + i) =
+                make_uint4(lo4(a.x, a.y), lo4(a.z, a.w), lo4(b.x, b.y), lo4(b.z, b.w));
+    } else {
+        for (int64_t j = i; j < n; ++j) {
+            y0[j] = (uint8_t)(x[j] >> 8);
+            if (y1) y1[j] = (uint8_t)(x[j] & 0xFFu);
+        }
+    }
+}
+
+hipError_t launch_hbm_rate(const uint16_t* x, int64_t n, uint8_t* y0, uint8_t* y1,
+                           hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    const int64_t blocks = (n + 4095) / 4096;
+    return launch(hbm_rate_kernel, dim3((unsigned)blocks), dim3(256), stream, x, n, y0, y1);
 }
 
 }  // namespace fp8bs

@@ -229,6 +229,20 @@ fp8bs_status fp8_encode_e4m3(const float* x, int64_t n, uint8_t* q, fp8bs_stream
  */
 fp8bs_status fp8bs_mfma_rate(float* out, int64_t blocks, int iters, float v, fp8bs_stream_t stream);
 
+/*
+ * Diagnostic, outside the FP8 path: the HBM streaming rate of the
+ * quantizers' access pattern without their arithmetic, against which their
+ * bandwidth can be priced.  Reads n BF16 values and writes one byte per
+ * value to y0 (its high byte) and, when y1 is not NULL, one more to y1 (its
+ * low byte): 2 bytes read and 1 (row-tile or token-axis quantizer) or 2
+ * (dual-axis quantizer) bytes written per element, in 16-byte accesses.
+ *   x bf16 [n], y0 u8 [n], y1 u8 [n] or NULL; all 16-byte aligned device
+ *   memory, caller-owned.  n >= 0 (FP8BS_ERR_SHAPE otherwise).
+ * Asynchronous on stream: time it with events recorded on the same stream.
+ */
+fp8bs_status fp8bs_hbm_rate(const uint16_t* x, int64_t n, uint8_t* y0, uint8_t* y1,
+                            fp8bs_stream_t stream);
+
 /* Static string naming a status (never NULL). */
 const char* fp8bs_status_string(fp8bs_status status);
 

@@ -30,7 +30,7 @@ def L():
 
 def test_exports_every_header_symbol(L):
     names = header_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -135,6 +135,16 @@ def test_bf16_gemm_argument_errors(L):
     assert f(None, None, None, 1, 0, 128, 128, None) == OK
 
 
+def test_hbm_rate_argument_errors(L):
+    f = L.fp8bs_hbm_rate
+    assert f(A16, -1, A16, None, None) == SHAPE
+    assert f(None, 4, A16, None, None) == NULL
+    assert f(A16, 4, None, None, None) == NULL
+    assert f(MIS, 4, A16, None, None) == ALIGN
+    assert f(A16, 4, A16, MIS, None) == ALIGN
+    assert f(None, 0, None, None, None) == OK
+
+
 def test_mfma_rate_argument_errors(L):
     f = L.fp8bs_mfma_rate
     assert f(A16, -1, 10, 0.125, None) == SHAPE
@@ -172,3 +182,59 @@ def test_fp8_linear_has_no_cpu_path():
         lin(torch.randn(128, 256).bfloat16())
     with pytest.raises(ValueError):
         pkg.Fp8Linear(200, 128)
+
+
+def _no_library(monkeypatch):
+    """Make any call into the C library fail the test: the checks below must
+    reject their inputs before one is made."""
+    def boom():
+        raise AssertionError("the library was reached")
+    monkeypatch.setattr(B, "capi", boom)
+
+
+def test_binding_rejects_mismatched_inputs_before_any_call(monkeypatch):
+    import torch
+
+    _no_library(monkeypatch)
+    u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+    E = lambda shape, dt: torch.zeros(shape, dtype=dt)
+    xq, xs = E((256, 256), u8), E((256, 2), f32)
+    wq, ws = E((128, 256), u8), E((1, 2), f32)
+    cases = [
+        ("wq", lambda: B.fp8_gemm_fprop(xq, xs, E((128, 128), u8), ws)),          # K differs
+        ("ws", lambda: B.fp8_gemm_fprop(xq, xs, wq, E((2, 2), f32))),
+        ("xq scales", lambda: B.fp8_gemm_fprop(xq, E((256, 1), f32), wq, ws)),
+        ("xq", lambda: B.fp8_gemm_fprop(E((256, 256), f32), xs, wq, ws)),         # dtype
+        ("xq", lambda: B.fp8_gemm_fprop(xq.t(), xs, wq, ws)),                      # strided
+        ("wq_t", lambda: B.fp8_gemm_dgrad(xq, xs, E((128, 128), u8), ws)),
+        ("ws", lambda: B.fp8_gemm_dgrad(xq, xs, E((128, 256), u8), E((1, 1), f32))),
+        ("dyq scales", lambda: B.fp8_gemm_dgrad_quantized(xq, E((255, 2), f32), E((128, 256), u8), ws)),
+        ("xtq", lambda: B.fp8_gemm_wgrad(xq, xs, E((128, 128), u8), E((128, 2), f32))),
+        ("xts", lambda: B.fp8_gemm_wgrad(xq, xs, E((128, 256), u8), E((128, 1), f32))),
+        ("dytq", lambda: B.fp8_gemm_wgrad(E((256,), u8), xs, E((128, 256), u8), E((128, 2), f32))),
+        ("b", lambda: B.bf16_gemm_tn(E((128, 256), bf), E((128, 128), bf))),
+        ("a", lambda: B.bf16_gemm_tn(E((128, 256), f32), E((128, 256), bf))),
+        ("x", lambda: B.fp8_quantize_rowtile(E((128, 256), bf).t())),
+        ("x", lambda: B.fp8_quantize_block(E((128, 256), f32))),
+        ("x", lambda: B.fp8_quantize_transposed(E((128, 256, 1), bf))),
+        ("x", lambda: B.fp8_quantize_dual(E((256, 128), bf)[:, ::2])),
+        ("output", lambda: B.fp8_gemm_fprop(xq, xs, wq, ws, y=E((256, 64), bf))),
+        ("workspace", lambda: B.fp8_gemm_wgrad(xq, xs, E((128, 256), u8), E((128, 2), f32),
+                                               workspace=E((64,), f32))),
+    ]
+    for what, call in cases:
+        with pytest.raises(ValueError, match=what):
+            call()
+
+
+def test_binding_rejects_host_tensors_before_any_call(monkeypatch):
+    import torch
+
+    _no_library(monkeypatch)
+    with pytest.raises(ValueError, match="device tensor"):
+        B.fp8_quantize_rowtile(torch.zeros((128, 256), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="device tensor"):
+        B.fp8_gemm_fprop(torch.zeros((128, 256), dtype=torch.uint8),
+                         torch.zeros((128, 2), dtype=torch.float32),
+                         torch.zeros((128, 256), dtype=torch.uint8),
+                         torch.zeros((1, 2), dtype=torch.float32))

@@ -32,3 +32,19 @@ def test_mfma_rate_is_plausible():
     tflops = blocks * 4 * iters * 128 * 16384 / (e0.elapsed_time(e1) / 1e3) / 1e12
     print(f"mfma_rate {tflops:.0f} TFLOP/s on {cus} CUs", flush=True)
     assert 1000 < tflops < 2600
+
+
+@pytest.mark.parametrize("n", [0, 5, 4096, 4096 * 37 + 23])
+def test_hbm_rate_kernel_moves_the_bytes(n):
+    """The streaming probe writes the high byte (and, with two outputs, the
+    low byte) of every input value, including a ragged tail."""
+    print(f"hbm rate n={n}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(n)
+    x = torch.randint(-32768, 32767, (n,), dtype=torch.int16, device="cuda", generator=g)
+    y0, y1 = fp8.fp8bs_hbm_rate(x, two_outputs=True)
+    z0, z1 = fp8.fp8bs_hbm_rate(x)
+    torch.cuda.synchronize()
+    u = x.to(torch.int32) & 0xFFFF
+    assert torch.equal(y0.to(torch.int32), u >> 8)
+    assert torch.equal(y1.to(torch.int32), u & 0xFF)
+    assert z1 is None and torch.equal(z0, y0)

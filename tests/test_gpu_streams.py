@@ -83,3 +83,35 @@ def test_gemms_run_on_the_callers_stream():
         for a, b in zip(g, w_):
             assert _same(a, b)
     assert np.isfinite(got[0].float().cpu().numpy()).all()
+
+
+def test_temporaries_of_a_stream_argument_live_on_that_stream():
+    """A call given stream= (not the current stream) allocates its output and
+    its "auto" workspace on that stream, so torch does not hand the freed
+    workspace to other work while the split-K kernels still use it: the
+    allocator's segments holding them are tagged with the launch stream, and
+    an immediate same-size allocation on the current stream, written at
+    once, leaves the result unchanged."""
+    M, N, K = 4096, 1024, 1024
+    dytq = torch.randint(0, 0x7E, (N, M), dtype=torch.uint8, device="cuda")
+    xtq = torch.randint(0, 0x7E, (K, M), dtype=torch.uint8, device="cuda")
+    dyts = torch.rand(N, M // 128, device="cuda") + 0.5
+    xts = torch.rand(K, M // 128, device="cuda") + 0.5
+    nbytes = fp8.fp8_gemm_wgrad_workspace_bytes(M, N, K)
+    assert nbytes > 0, "the shape must split for this test"
+    want = fp8.fp8_gemm_wgrad(dytq, dyts, xtq, xts, workspace="auto")
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    print("wgrad with stream= a side stream behind a spin", flush=True)
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(SPIN_CYCLES)
+    got = fp8.fp8_gemm_wgrad(dytq, dyts, xtq, xts, workspace="auto", stream=side)
+    junk = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")   # current stream
+    segs = torch.cuda.memory_snapshot()
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert _same(got, want)
+    side_blocks = [b["size"] for s in segs if s["stream"] == side.cuda_stream for b in s["blocks"]]
+    assert any(sz >= nbytes for sz in side_blocks), side_blocks
+    assert any(sz >= N * K * 4 for sz in side_blocks), side_blocks
+    del junk
