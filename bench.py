@@ -162,6 +162,8 @@ def parse():
                     help="skip the measurements of the layer-level comparisons that follow the "
                          "step (for profiler runs, whose kernel statistics should hold the step "
                          "alone)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration measurements of configurations 1-4")
     ap.add_argument("--summarize-rocprof", metavar="DIR",
                     help="print a text summary of rocprofv3 CSV output in DIR and exit")
     return ap.parse_args()
@@ -381,7 +383,7 @@ def cpu_baseline(fraction: int, gpu=None):
             results.append((g, rows, (dq, ds), (xq, xs), y))
     secs = time.perf_counter() - t0
     baseline = {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
-                "kind": "oracle",
+                "cpu": cpu_model(), "kind": "oracle",
                 "sample": f"layer 0 of the 28-layer linear set: all 12 GEMMs on 1/{fraction} of "
                           f"their output rows ({flops / 1e9:.1f} GFLOP) plus the quantization "
                           f"those rows need; {secs:.1f} s wall"}
@@ -390,11 +392,26 @@ def cpu_baseline(fraction: int, gpu=None):
     return baseline, _parity_against_oracle(np, oracle, gpu, results)
 
 
+def bf16_gate(np, oracle, out_bits, ref_f32, a_deq, b_deq):
+    """Per-element pass mask of BF16 outputs: within one BF16 ulp of the
+    rounded oracle value; only where the oracle value is itself no larger
+    than the FP32 bound 1e-4 ||a_i|| ||b_j|| may it differ by that bound plus
+    one ulp of the larger value (an FP32-level difference spans many ulps of
+    so small a value)."""
+    got = oracle.bf16_to_f32(out_bits).astype(np.float64)
+    r = oracle.bf16_to_f32(oracle.f32_to_bf16(ref_f32)).astype(np.float64)
+    tiny = np.finfo(np.float32).tiny
+    ulp = lambda v: np.exp2(np.floor(np.log2(np.maximum(np.abs(v), tiny))) - 7)
+    bound = 1e-4 * np.outer(np.linalg.norm(a_deq, axis=1), np.linalg.norm(b_deq, axis=1))
+    err = np.abs(got - r)
+    near_zero = np.abs(np.asarray(ref_f32, np.float64)) <= bound
+    return (err <= ulp(r)) | (near_zero & (err <= bound + ulp(np.maximum(np.abs(r), np.abs(got)))))
+
+
 def _parity_against_oracle(np, oracle, gpu, results):
     """Codes and scales must match bit for bit; FP32 outputs relF <= 1e-5 and
     |err| <= 1e-4 ||a_i|| ||b_j|| (dequantized contraction vectors); BF16
-    outputs within one BF16 ulp of the rounded oracle value, or within that
-    bound plus half an ulp."""
+    outputs as bf16_gate."""
     codes_ok = True
     gemms = {}
     for g, rows, qa, qb, y in results:
@@ -411,14 +428,8 @@ def _parity_against_oracle(np, oracle, gpu, results):
                 codes_ok &= np.array_equal(wqt, qb[1])
                 w_deq = np.ascontiguousarray(w_deq.T)
             out = gpu["out"][g.name][rows]
-            ref_bits = oracle.f32_to_bf16(y)
             got = oracle.bf16_to_f32(out).astype(np.float64)
-            ref = oracle.bf16_to_f32(ref_bits).astype(np.float64)
-            mag = np.maximum(np.abs(ref), np.finfo(np.float32).tiny)
-            ulp = np.exp2(np.floor(np.log2(mag)) - 7)
-            bound = 1e-4 * np.outer(np.linalg.norm(a_deq, axis=1), np.linalg.norm(w_deq, axis=1))
-            err = np.abs(got - ref)
-            ok = (err <= ulp) | (err <= bound + 0.5 * ulp)
+            ok = bf16_gate(np, oracle, out, y, a_deq, w_deq)
             gemms[g.name] = {"out": "bf16", "elements": int(ok.size),
                              "within_gate": bool(ok.all()),
                              "relF_vs_fp32_oracle": float(f"{oracle.rel_frobenius(got, y):.3e}")}
@@ -461,6 +472,262 @@ def gpu_layer0(torch, plan, ops):
 
 LAYER_LINEARS = [("qkv", 2048, 4096), ("o", 2048, 2048), ("gate_up", 2048, 12288),
                  ("down", 6144, 2048)]
+
+FLUSH_BYTES = 512 << 20       # > the 256 MB last-level cache
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def parse_sclk_json(text: str):
+    """Graphics clocks (MHz) found in amd-smi ("gfx_N" clock entries) or
+    rocm-smi ("sclk clock speed") JSON output, or None."""
+    import re
+    start = min((i for i in (text.find("{"), text.find("[")) if i >= 0), default=-1)
+    if start < 0:
+        return None
+    try:
+        data = json.loads(text[start:])
+    except ValueError:
+        return None
+    found = []
+
+    def walk(o, path):
+        if isinstance(o, dict):
+            for k, v in o.items():
+                walk(v, path + [str(k).lower()])
+        elif isinstance(o, list):
+            for v in o:
+                walk(v, path)
+        else:
+            key = " ".join(path)
+            if (re.search(r"\bgfx_\d+ clk value$", key) or "sclk clock speed" in key):
+                m = re.search(r"(\d+(?:\.\d+)?)", str(o))
+                if m:
+                    found.append(float(m.group(1)))
+
+    walk(data, [])
+    return found or None
+
+
+def _sclk_from_smi():
+    """Current graphics clocks in MHz reported by amd-smi or rocm-smi (a list,
+    one per GPU), or None when neither answers."""
+    import subprocess
+    for cmd in (["amd-smi", "metric", "--clock", "--json"], ["rocm-smi", "--showclocks", "--json"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+        except (OSError, subprocess.SubprocessError):
+            continue
+        if r.returncode == 0:
+            v = parse_sclk_json(r.stdout)
+            if v:
+                return v
+    return None
+
+
+class SclkSampler:
+    """Samples the graphics clock from the SMI tools in a background thread
+    (the tool runs as a child process; the GIL is released while waiting)."""
+
+    def __init__(self, period_s: float = 0.5):
+        import threading
+        self.period = period_s
+        self.samples = []
+        self.stop = threading.Event()
+        self.thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self.stop.is_set():
+            v = _sclk_from_smi()
+            if v is None:
+                return
+            self.samples.append(max(v))
+            self.stop.wait(self.period)
+
+    def __enter__(self):
+        self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        self.thread.join(timeout=30)
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"samples": len(v), "min_mhz": v[0], "median_mhz": v[len(v) // 2], "max_mhz": v[-1]}
+
+
+class Timer:
+    """Median kernel time of fn over reps iterations, each preceded by a
+    write of a 512 MiB scratch buffer (outside the timed events) so the
+    last-level cache holds nothing of the inputs; events are recorded on the
+    current stream, the one the library calls are enqueued on."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+
+    def median_ms(self, fn, reps=25, warmup=3):
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for i, (a, b) in enumerate(ev):
+            self.flush.fill_(i & 0xFF)
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in ev)
+        return t[len(t) // 2]
+
+
+def hbm_ceiling(torch, fp8, timer, n: int, two_outputs: bool) -> float:
+    """GB/s of the library's streaming probe moving the quantizers' bytes
+    (2 read + 1 or 2 written per element) for n elements, cache flushed."""
+    x = torch.empty(n, dtype=torch.int16, device="cuda").fill_(0x3F80)
+    y0 = torch.empty(n, dtype=torch.uint8, device="cuda")
+    y1 = torch.empty(n, dtype=torch.uint8, device="cuda") if two_outputs else None
+    ms = timer.median_ms(lambda: fp8.fp8bs_hbm_rate(x, y0, y1), reps=15)
+    return n * (4 if two_outputs else 3) / (ms / 1e3) / 1e9
+
+
+def _config_ops(torch, fp8, cfg_name, inputs):
+    """(name, kind, fn, units) for every kernel a configuration runs, on
+    device tensors of its seeded inputs (units: bytes or flops)."""
+    c = inputs.CONFIGS[cfg_name]
+    dev = {n: torch.from_numpy(inputs.tensor(cfg_name, n).view("int16")).view(torch.bfloat16)
+           .to("cuda") for n in c.tensors}
+    ops = []
+    done = set()
+    for g in c.gemms:
+        a, b = dev[g.a], dev[g.b]
+        if g.kind in ("fprop", "dgrad"):
+            M, L = a.shape
+            q, s = fp8.fp8_quantize_rowtile(a)
+            if ("row", g.a) not in done:
+                ops.append((f"{g.a}.rowtile", "quant_rowtile",
+                            lambda a=a, q=q, s=s: fp8.fp8_quantize_rowtile(a, q, s),
+                            M * L * 3 + M * (L // 128) * 4))
+                done.add(("row", g.a))
+            N, K = b.shape
+            wq, wqt, ws = fp8.fp8_quantize_block(b, with_transpose=(g.kind == "dgrad"))
+            if ("block", g.b, g.kind) not in done:
+                ops.append((f"{g.b}.block", "quant_block",
+                            lambda b=b, wq=wq, wqt=wqt, ws=ws: fp8.fp8_quantize_block(
+                                b, wq, wqt, ws, with_transpose=wqt is not None),
+                            N * K * (4 if g.kind == "dgrad" else 3) + (N // 128) * (K // 128) * 4))
+                done.add(("block", g.b, g.kind))
+            out = torch.float32 if g.out == "f32" else torch.bfloat16
+            if g.kind == "fprop":
+                y = torch.empty(g.M, g.N, dtype=out, device="cuda")
+                fn = lambda q=q, s=s, wq=wq, ws=ws, y=y, o=out: fp8.fp8_gemm_fprop(q, s, wq, ws, o, y)
+            else:
+                y = torch.empty(g.M, g.K, dtype=out, device="cuda")
+                fn = lambda q=q, s=s, wqt=wqt, ws=ws, y=y, o=out: fp8.fp8_gemm_dgrad(q, s, wqt, ws, o, y)
+            ops.append((g.name, "gemm_" + g.kind, fn, g.flops))
+        else:
+            tq = {}
+            for nm, x in ((g.a, a), (g.b, b)):
+                M, C = x.shape
+                qt, st = fp8.fp8_quantize_transposed(x)
+                tq[nm] = (qt, st)
+                ops.append((f"{nm}.transposed", "quant_transposed",
+                            lambda x=x, qt=qt, st=st: fp8.fp8_quantize_transposed(x, qt, st),
+                            M * C * 3 + C * (M // 128) * 4))
+            dyt, dyts = tq[g.a]
+            xt, xts = tq[g.b]
+            dw = torch.empty(g.N, g.K, dtype=torch.float32, device="cuda")
+            nb = fp8.fp8_gemm_wgrad_workspace_bytes(g.M, g.N, g.K)
+            wsp = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
+            ops.append((g.name, "gemm_wgrad",
+                        lambda dyt=dyt, dyts=dyts, xt=xt, xts=xts, dw=dw, wsp=wsp:
+                        fp8.fp8_gemm_wgrad(dyt, dyts, xt, xts, dw, wsp), g.flops))
+    return ops
+
+
+def _oracle_config_seconds(cfg_name, inputs, cores):
+    """Wall seconds of the oracle computing a configuration in full (its
+    quantizations and every GEMM), on `cores` threads."""
+    import oracle
+    c = inputs.CONFIGS[cfg_name]
+    host = {n: inputs.tensor(cfg_name, n) for n in c.tensors}
+    t0 = time.perf_counter()
+    for g in c.gemms:
+        a, b = host[g.a], host[g.b]
+        if g.kind in ("fprop", "dgrad"):
+            q, s = oracle.quantize_rowtile(a, threads=cores)
+            wq, wqt, ws = oracle.quantize_block(b, with_transpose=(g.kind == "dgrad"), threads=cores)
+            if g.kind == "fprop":
+                oracle.gemm_fprop(q, s, wq, ws, threads=cores)
+            else:
+                oracle.gemm_dgrad(q, s, wqt, ws, threads=cores)
+        else:
+            dq, ds = oracle.quantize_transposed(a, threads=cores)
+            xq, xs = oracle.quantize_transposed(b, threads=cores)
+            oracle.gemm_wgrad(dq, ds, xq, xs, threads=cores)
+    return time.perf_counter() - t0
+
+
+def config_measurements(torch, fp8, inputs, timer, ceilings, with_oracle: bool):
+    """Configurations 1-4 (Tiny, QKV, MLP pair, down backward), each kernel
+    timed alone with the cache flushed before every iteration (median of 25),
+    and the oracle's time for the whole configuration on all host cores."""
+    cores = len(os.sched_getaffinity(0))
+    out = {}
+    for cfg_name in ("tiny", "qkv", "mlp", "down_bwd"):
+        ops = _config_ops(torch, fp8, cfg_name, inputs)
+        torch.cuda.synchronize()
+        kern = {}
+        gemm_ms = quant_ms = 0.0
+        flops = qbytes = 0
+        for name, kind, fn, units in ops:
+            ms = timer.median_ms(fn)
+            e = {"kind": kind, "us": round(ms * 1e3, 2)}
+            if kind.startswith("gemm"):
+                tf = units / (ms / 1e3) / 1e12
+                e.update(tflops=round(tf, 1), frac_f16_peak=round(tf / PEAK_F16_TFLOPS, 4),
+                         pct_fp8_peak=round(100 * tf / PEAK_FP8_TFLOPS, 2))
+                gemm_ms += ms
+                flops += units
+            else:
+                gbs = units / (ms / 1e3) / 1e9
+                ceil = ceilings["write1"]
+                e.update(gbs=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4),
+                         frac_of_probe=round(gbs / ceil, 4))
+                quant_ms += ms
+                qbytes += units
+            kern[name] = e
+        line = {"kernels": kern,
+                "gemm_tflops": round(flops / (gemm_ms / 1e3) / 1e12, 1),
+                "gemm_frac_f16_peak": round(flops / (gemm_ms / 1e3) / 1e12 / PEAK_F16_TFLOPS, 4),
+                "quant_gbs": round(qbytes / (quant_ms / 1e3) / 1e9, 1),
+                "quant_frac_hbm_peak": round(qbytes / (quant_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
+        if cfg_name == "tiny":
+            line["note"] = "67 MFLOP and 0.4 MB per call: launch-bound, exempt from the roofline gates"
+        if with_oracle:
+            secs = _oracle_config_seconds(cfg_name, inputs, cores)
+            gpu_s = (gemm_ms + quant_ms) / 1e3
+            line["oracle"] = {"seconds": round(secs, 2), "cores": cores, "cpu": cpu_model(),
+                              "gflops": round(flops / secs / 1e9, 2),
+                              "gpu_speedup": round(secs / gpu_s, 1)}
+        out[cfg_name] = line
+        del ops
+        torch.cuda.empty_cache()
+    return out
 
 
 def _time_events(torch, fn, reps):
@@ -523,7 +790,8 @@ def bf16_comparison(torch, fp8, cfg, fp8_ms_per_layer, reps=5):
         "fp8_ms_per_layer": round(fp8_ms_per_layer, 3),
         "fp8_tflops": round(flops / fp8_ms_per_layer / 1e9, 1),
         "fp8_speedup_vs_own_bf16": round(own / fp8_ms_per_layer, 3),
-        "torch_bf16_ms_per_layer": round(blas, 3), "torch_bf16_tflops": round(flops / blas / 1e9, 1)}}
+        "torch_bf16_ms_per_layer": round(blas, 3), "torch_bf16_tflops": round(flops / blas / 1e9, 1),
+        "fp8_speedup_vs_best_bf16": round(min(own, blas) / fp8_ms_per_layer, 3)}}
 
 
 def dgrad_epilogue_quantization(torch, fp8, cfg, reps=5):
@@ -641,11 +909,12 @@ def main():
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)]
               for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        run_step(ops, events[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with SclkSampler() as sclk:
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            run_step(ops, events[s])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
 
     # per-kind device time from the events bracketing every launch
     kinds = {}
@@ -665,6 +934,17 @@ def main():
     value = gemm_flops / (wall / args.steps) / 1e12
 
     breakdown = kind_summary(kinds, args.steps)
+    # the quantizers' own ceiling: the library's streaming probe moving the
+    # same bytes per element (2 read, 1 or 2 written) over the largest tensor
+    # of the step, cache flushed
+    timer = Timer(torch)
+    n_big = max(x.numel() for x in plan.act.values())
+    ceilings = {"write1": hbm_ceiling(torch, fp8, timer, n_big, False),
+                "write2": hbm_ceiling(torch, fp8, timer, n_big, True)}
+    for kind, v in breakdown.items():
+        if not kind.startswith("gemm"):
+            c = ceilings["write2" if kind == "quant_dual" else "write1"]
+            v["frac_of_probe"] = round(v["rate"] / c, 4)
     dom = next(iter(breakdown))
     d = breakdown[dom]
     dom_is_gemm = dom.startswith("gemm")
@@ -716,8 +996,24 @@ def main():
     }
     if standalone:
         result["kernels_outside_step"] = kind_summary(standalone, 1)
+        for kind, v in result["kernels_outside_step"].items():
+            v["frac_of_probe"] = round(v["rate"] / ceilings["write1"], 4)
+    result["hbm_probe"] = {
+        "what": "fp8bs_hbm_rate: 2 bytes read and 1 (write1) or 2 (write2) bytes written per "
+                "element in 16-byte accesses, %d elements, last-level cache flushed, median" % n_big,
+        "write1_gbs": round(ceilings["write1"], 1), "write2_gbs": round(ceilings["write2"], 1),
+        "write1_frac_hbm_peak": round(ceilings["write1"] / PEAK_HBM_GBS, 4),
+        "write2_frac_hbm_peak": round(ceilings["write2"] / PEAK_HBM_GBS, 4)}
+    result["sclk"] = sclk.summary()
+    if roofline.get("peak_at_clock"):
+        # the clock the MFMA-only kernel implies: 2.5 PFLOP/s is the spec at 2.4 GHz
+        result["sclk_from_mfma_rate_mhz"] = round(roofline["peak_at_clock"] / PEAK_F16_TFLOPS * 2400)
+    if not args.no_configs:
+        result["configs"] = config_measurements(torch, fp8, inputs, timer, ceilings,
+                                                not args.no_cpu_baseline)
     # the GPU's own layer-0 results, compared with the oracle's in the cpu_baseline leg
     layer0 = None if args.no_cpu_baseline else gpu_layer0(torch, plan, ops)
+    del timer
     if not args.no_next_rows:
         cfg_obj, cfg_layers = plan.cfg, plan.cfg.layers
         del plan, ops, events

@@ -87,3 +87,18 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
                        text=True, timeout=60)
     assert r.returncode == 2 and "one GPU" in r.stdout
+
+
+def test_sclk_parsing_of_both_smi_tools():
+    amd = ('[{"gpu": 0, "clock": {"gfx_0": {"clk": {"value": 2100, "unit": "MHz"}, '
+           '"min_clk": {"value": 500, "unit": "MHz"}}, "gfx_1": {"clk": {"value": 2095, '
+           '"unit": "MHz"}}, "mem_0": {"clk": {"value": 1900, "unit": "MHz"}}}}]')
+    assert bench.parse_sclk_json(amd) == [2100.0, 2095.0]
+    rocm = 'WARNING: x\n{"card0": {"sclk clock speed:": "(2400Mhz)", "mclk clock speed:": "(1900Mhz)"}}'
+    assert bench.parse_sclk_json(rocm) == [2400.0]
+    assert bench.parse_sclk_json("no json here") is None
+    assert bench.parse_sclk_json('{"card0": {"fclk clock speed:": "(1000Mhz)"}}') is None
+
+
+def test_cpu_model_is_a_string():
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
