@@ -26,18 +26,29 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the same
+# sources (the argument checks of the C ABI run under them; device code is
+# built as usual).  Loaded only by the C-ABI CPU tests, with clang's ASan
+# runtime preloaded.
+ASAN_LIB = os.path.join(PKG, "libfp8bs_asan.so")
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-shared-libsan",
+                  "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-o", tmp, *srcs]
+    out = ASAN_LIB if sanitize else LIB
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *(SANITIZE_FLAGS if sanitize else []), "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libfp8bs.so")
-    os.replace(tmp, LIB)
-    return LIB
+        raise RuntimeError(f"hipcc failed building {os.path.basename(out)}")
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

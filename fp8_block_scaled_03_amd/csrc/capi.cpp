@@ -70,6 +70,18 @@ fp8bs_status check_ptr(const void* p, bool empty, size_t align) {
 
 fp8bs_status launched(hipError_t e) { return e == hipSuccess ? FP8BS_OK : FP8BS_ERR_HIP; }
 
+// The integer a caller passed for an enum parameter.  A C caller may pass any
+// int there; in C++ an enum object holding a value outside its enumerators'
+// range may not be read as the enum, so the value is read through its object
+// representation instead.
+template <typename E>
+int enum_value(const E& e) {
+    static_assert(sizeof(E) == sizeof(int), "C enums are int-sized");
+    int v;
+    std::memcpy(&v, &e, sizeof v);
+    return v;
+}
+
 }  // namespace
 
 extern "C" {
@@ -77,7 +89,7 @@ extern "C" {
 int fp8bs_version(void) { return 200; }
 
 const char* fp8bs_status_string(fp8bs_status status) {
-    switch (status) {
+    switch (enum_value(status)) {
         case FP8BS_OK: return "ok";
         case FP8BS_ERR_NULL: return "null pointer";
         case FP8BS_ERR_SHAPE: return "invalid shape (negative, or not a multiple of 128)";
@@ -173,7 +185,8 @@ fp8bs_status fp8_gemm_fprop(const uint8_t* xq, const float* xs, const uint8_t* w
                             void* y, fp8bs_out_dtype yt, int64_t M, int64_t N, int64_t K,
                             fp8bs_stream_t stream) {
     if (M < 0 || !mult128(N) || !mult128(K)) return FP8BS_ERR_SHAPE;
-    return gemm_common(fp8bs::kScaleBlock, xq, xs, wq, ws, y, (int)yt, M, N, K, nullptr, 0, stream);
+    return gemm_common(fp8bs::kScaleBlock, xq, xs, wq, ws, y, enum_value(yt), M, N, K, nullptr, 0,
+                       stream);
 }
 
 fp8bs_status fp8_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wq_t,
@@ -181,8 +194,8 @@ fp8bs_status fp8_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t*
                             int64_t K, fp8bs_stream_t stream) {
     if (M < 0 || !mult128(N) || !mult128(K)) return FP8BS_ERR_SHAPE;
     // TN form: rows of dY (contraction N) against rows of W^T ([K, N]).
-    return gemm_common(fp8bs::kScaleBlockT, dyq, dys, wq_t, ws, dx, (int)dxt, M, K, N, nullptr, 0,
-                       stream);
+    return gemm_common(fp8bs::kScaleBlockT, dyq, dys, wq_t, ws, dx, enum_value(dxt), M, K, N,
+                       nullptr, 0, stream);
 }
 
 fp8bs_status fp8_gemm_dgrad_quantized(const uint8_t* dyq, const float* dys, const uint8_t* wq_t,
@@ -225,7 +238,8 @@ size_t fp8_gemm_wgrad_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 fp8bs_status bf16_gemm_tn(const uint16_t* a, const uint16_t* b, void* c, fp8bs_out_dtype ct,
                           int64_t I, int64_t J, int64_t K, fp8bs_stream_t stream) {
     if (I < 0 || !mult128(J) || !mult128(K)) return FP8BS_ERR_SHAPE;
-    if ((int)ct != FP8BS_OUT_F32 && (int)ct != FP8BS_OUT_BF16) return FP8BS_ERR_DTYPE;
+    const int cv = enum_value(ct);
+    if (cv != FP8BS_OUT_F32 && cv != FP8BS_OUT_BF16) return FP8BS_ERR_DTYPE;
     const bool out_empty = (I == 0 || J == 0);
     const bool in_empty = out_empty || K == 0;
     FP8BS_TRY(check_ptr(a, in_empty, 16));
@@ -234,7 +248,7 @@ fp8bs_status bf16_gemm_tn(const uint16_t* a, const uint16_t* b, void* c, fp8bs_o
     if (out_empty) return FP8BS_OK;
     int cus;
     FP8BS_TRY(check_device(&cus));
-    return launched(fp8bs::launch_gemm_bf16(a, b, c, ct == FP8BS_OUT_BF16, I, J, K, stream));
+    return launched(fp8bs::launch_gemm_bf16(a, b, c, cv == FP8BS_OUT_BF16, I, J, K, stream));
 }
 
 fp8bs_status fp8_encode_e4m3(const float* x, int64_t n, uint8_t* q, fp8bs_stream_t stream) {

@@ -22,6 +22,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle_fp8bs.so")
+# AddressSanitizer + UndefinedBehaviorSanitizer build of the same source, for
+# a host sanitizer run of the CPU tests (FP8BS_ORACLE_SANITIZE=1, with gcc's
+# libasan and libubsan preloaded into the Python process).
+ASAN_LIB_PATH = os.path.join(_HERE, "liboracle_fp8bs_asan.so")
 SRC_PATH = os.path.join(_HERE, "fp8bs_oracle.c")
 
 MODE_BLOCK = 0     # fprop: weight scales ws[j/128][kb]
@@ -31,15 +35,22 @@ MODE_ROW = 2       # wgrad: per-row token-axis scales s[j][kb]
 _ERRORS = {-1: "shape", -2: "non-finite input", -3: "argument", -4: "out of memory"}
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (no fast-math, no FP contraction)."""
-    if force or not os.path.exists(LIB_PATH) or (
-            os.path.getmtime(LIB_PATH) < os.path.getmtime(SRC_PATH)):
-        cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC",
-               "-shared", "-std=c11", "-Wall", "-o", LIB_PATH + ".tmp", SRC_PATH, "-lm"]
+def _sanitized() -> bool:
+    return os.environ.get("FP8BS_ORACLE_SANITIZE", "") == "1"
+
+
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile the oracle with gcc (no fast-math, no FP contraction); with
+    sanitize, the ASan/UBSan build (-O1, every UB report fatal)."""
+    out = ASAN_LIB_PATH if sanitize else LIB_PATH
+    if force or not os.path.exists(out) or (os.path.getmtime(out) < os.path.getmtime(SRC_PATH)):
+        opt = (["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                "-fno-sanitize-recover=all"] if sanitize else ["-O2"])
+        cmd = ["gcc", *opt, "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC",
+               "-shared", "-std=c11", "-Wall", "-o", out + ".tmp", SRC_PATH, "-lm"]
         subprocess.run(cmd, check=True)
-        os.replace(LIB_PATH + ".tmp", LIB_PATH)
-    return LIB_PATH
+        os.replace(out + ".tmp", out)
+    return out
 
 
 _lib = None
@@ -48,9 +59,10 @@ _lib = None
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(SRC_PATH):
-            build()
-        L = ctypes.CDLL(LIB_PATH)
+        path = ASAN_LIB_PATH if _sanitized() else LIB_PATH
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(SRC_PATH):
+            build(sanitize=_sanitized())
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i64 = ctypes.c_int64
         L.oracle_e4m3_value.restype = ctypes.c_double

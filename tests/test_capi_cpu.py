@@ -23,6 +23,15 @@ def header_functions():
 
 @pytest.fixture(scope="module")
 def L():
+    """The library under test: the built libfp8bs.so, or, when FP8BS_CAPI_LIB
+    names one, that build of it (the host-sanitizer build)."""
+    alt = os.environ.get("FP8BS_CAPI_LIB")
+    if alt:
+        lib = ctypes.CDLL(alt)
+        for name, (res, args) in B.SIGNATURES.items():
+            getattr(lib, name).restype = res
+            getattr(lib, name).argtypes = args
+        return lib
     if not os.path.exists(B.LIB_PATH):
         pytest.fail("libfp8bs.so is not built (run __graft_entry__.build())")
     return B.capi()
