@@ -37,6 +37,7 @@ SIGNATURES = {
     "fp8_gemm_dgrad": (_INT, [_P, _P, _P, _P, _P, _INT, _I64, _I64, _I64, _P]),
     "fp8_gemm_dgrad_quantized": (_INT, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "fp8_gemm_wgrad": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
+    "fp8_gemm_wgrad_noalloc": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "fp8_gemm_wgrad_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64]),
     "bf16_gemm_tn": (_INT, [_P, _P, _P, _INT, _I64, _I64, _I64, _P]),
     "fp8_encode_e4m3": (_INT, [_P, _I64, _P, _P]),
@@ -333,6 +334,21 @@ def fp8_gemm_wgrad(dytq, dyts, xtq, xts, dw=None, workspace=None, stream=None):
     _check("fp8_gemm_wgrad", capi().fp8_gemm_wgrad(
         _ptr(dytq), _ptr(dyts), _ptr(xtq), _ptr(xts), _ptr(dw), M, N, K, ws_ptr, ws_bytes,
         _stream(dytq, stream)))
+    return dw
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20     # FP8BS_NOALLOC_SCRATCH_BYTES
+
+
+def fp8_gemm_wgrad_noalloc(dytq, dyts, xtq, xts, dw, stream=None):
+    """fp8_gemm_wgrad with its split-K slices in the library's static device
+    scratch: the C call allocates nothing, so dw (float32 [N,K]) must be
+    given.  Calls that may overlap on one device race on the scratch."""
+    M, N, K = _wgrad_operands(dytq, dyts, xtq, xts)
+    _need(dw, torch.float32, (N, K), "dw")
+    _on_device(dytq=dytq, dyts=dyts, xtq=xtq, xts=xts, dw=dw)
+    _check("fp8_gemm_wgrad_noalloc", capi().fp8_gemm_wgrad_noalloc(
+        _ptr(dytq), _ptr(dyts), _ptr(xtq), _ptr(xts), _ptr(dw), M, N, K, _stream(dytq, stream)))
     return dw
 
 

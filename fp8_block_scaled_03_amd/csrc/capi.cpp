@@ -228,6 +228,27 @@ fp8bs_status fp8_gemm_wgrad(const uint8_t* dytq, const float* dyts, const uint8_
                        workspace, workspace_bytes, stream);
 }
 
+fp8bs_status fp8_gemm_wgrad_noalloc(const uint8_t* dytq, const float* dyts, const uint8_t* xtq,
+                                    const float* xts, float* dw, int64_t M, int64_t N, int64_t K,
+                                    fp8bs_stream_t stream) {
+    if (!mult128(M) || !mult128(N) || !mult128(K)) return FP8BS_ERR_SHAPE;
+    const bool out_empty = (N == 0 || K == 0);
+    const bool in_empty = out_empty || M == 0;
+    FP8BS_TRY(check_ptr(dytq, in_empty, 16));
+    FP8BS_TRY(check_ptr(dyts, in_empty, 4));
+    FP8BS_TRY(check_ptr(xtq, in_empty, 16));
+    FP8BS_TRY(check_ptr(xts, in_empty, 4));
+    FP8BS_TRY(check_ptr(dw, out_empty, 16));
+    if (out_empty) return FP8BS_OK;
+    int cus;
+    FP8BS_TRY(check_device(&cus));
+    bool too_big = false;
+    const hipError_t e =
+        fp8bs::launch_wgrad_noalloc(dytq, dyts, xtq, xts, dw, M, N, K, cus, stream, &too_big);
+    if (too_big) return FP8BS_ERR_WORKSPACE;
+    return launched(e);
+}
+
 size_t fp8_gemm_wgrad_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (!mult128(M) || !mult128(N) || !mult128(K)) return 0;
     int cus = 0;

@@ -60,6 +60,15 @@ hipError_t launch_gemm_quantized(ScaleMode mode, const uint8_t* A, const float* 
                                  const uint8_t* B, const float* sB, uint16_t* C, uint8_t* Cq,
                                  float* Cs, int64_t I, int64_t J, int64_t Kc, hipStream_t stream);
 
+// wgrad exactly as launch_gemm(kScaleRow, ...) with a workspace of
+// gemm_workspace_bytes, the workspace being a static device array of
+// noalloc_scratch_bytes() (noalloc.hip).  Shapes needing more set *too_big
+// and launch nothing.
+size_t noalloc_scratch_bytes();
+hipError_t launch_wgrad_noalloc(const uint8_t* dytq, const float* dyts, const uint8_t* xtq,
+                                const float* xts, float* dw, int64_t M, int64_t N, int64_t K,
+                                int num_cus, hipStream_t stream, bool* too_big);
+
 // C[I, J] = A B^T with A [I, K], B [J, K] BF16 (unquantized comparator).
 hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* B, void* C, bool out_bf16,
                             int64_t I, int64_t J, int64_t K, hipStream_t stream);

@@ -171,6 +171,27 @@ fp8bs_status fp8_gemm_wgrad(const uint8_t* dytq, const float* dyts, const uint8_
                             const float* xts, float* dw, int64_t M, int64_t N, int64_t K,
                             void* workspace, size_t workspace_bytes, fp8bs_stream_t stream);
 
+/*
+ * fp8_gemm_wgrad without any allocation, for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The result is that of fp8_gemm_wgrad given a
+ * workspace of fp8_gemm_wgrad_workspace_bytes(M, N, K) bytes, bit for bit;
+ * the split-K slices live in a static device array of
+ * FP8BS_NOALLOC_SCRATCH_BYTES per device, allocated when the library is
+ * first used on a device and held until the process ends.
+ *   dytq, dyts, xtq, xts, dw, M, N, K: as fp8_gemm_wgrad (caller-owned).
+ * Errors as fp8_gemm_wgrad; a shape whose split needs more than
+ * FP8BS_NOALLOC_SCRATCH_BYTES returns FP8BS_ERR_WORKSPACE and launches
+ * nothing.  All calls on one device share its array and every call writes
+ * its slices before reading them: calls that may overlap in time on one
+ * device (different streams, different host threads) race on it and must be
+ * ordered by the caller.  The call allocates no device memory.
+ */
+#define FP8BS_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+fp8bs_status fp8_gemm_wgrad_noalloc(const uint8_t* dytq, const float* dyts, const uint8_t* xtq,
+                                    const float* xts, float* dw, int64_t M, int64_t N, int64_t K,
+                                    fp8bs_stream_t stream);
+
 /* Bytes of workspace fp8_gemm_wgrad uses for this shape on the current
  * device (16-byte aligned); 0 when it would not split.  Negative or invalid
  * shapes give 0. */

@@ -39,7 +39,7 @@ def L():
 
 def test_exports_every_header_symbol(L):
     names = header_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -117,6 +117,14 @@ def test_gemm_argument_errors(L):
     assert w(A16, A16, A16, A16, None, 128, 128, 128, None, 0, None) == NULL
     assert w(A16, A16, A16, A16, A16, 128, 128, 128, MIS, 64, None) == ALIGN
     assert w(None, None, None, None, None, 128, 0, 128, None, 0, None) == OK
+    n = L.fp8_gemm_wgrad_noalloc
+    assert n(A16, A16, A16, A16, A16, 100, 128, 128, None) == SHAPE
+    assert n(A16, A16, A16, A16, A16, 128, 128, 96, None) == SHAPE
+    assert n(A16, A16, None, A16, A16, 128, 128, 128, None) == NULL
+    assert n(A16, A16, A16, A16, None, 128, 128, 128, None) == NULL
+    assert n(A16, A16 + 2, A16, A16, A16, 128, 128, 128, None) == ALIGN
+    assert n(A16, A16, A16, A16, A16 + 8, 128, 128, 128, None) == ALIGN
+    assert n(None, None, None, None, None, 128, 0, 128, None) == OK
     assert L.fp8_gemm_wgrad_workspace_bytes(100, 128, 128) == 0
     assert L.fp8_gemm_wgrad_workspace_bytes(-128, 128, 128) == 0
 
