@@ -107,8 +107,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bs_fp8_kernel(
     tile_coords(blockIdx.x, tiles_i, tiles_j, &ti, &tj);
     const int64_t i0 = (int64_t)ti * kBM, j0 = (int64_t)tj * kBN;
     const int nkb_all = (int)(Kc / kBK);
-    const int kb0 = split_begin(blockIdx.y, p0, nps);
-    const int nkb = split_end(blockIdx.y, p0, nps, nkb_all) - kb0;
+    // only the row-scaled (wgrad) mode is ever split
+    const int kb0 = MODE == kScaleRow ? split_begin(blockIdx.y, p0, nps) : 0;
+    const int nkb = MODE == kScaleRow ? split_end(blockIdx.y, p0, nps, nkb_all) - kb0 : nkb_all;
     const int64_t jb_count = J / kBN;
 
     // Direct global -> LDS loads: wave w fills 1 KB pieces 4w .. 4w+3 of each
@@ -251,7 +252,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bs_fp8_kernel(
                 pk.y = pack_bf16x2(acc[it][jt][2], acc[it][jt][3]);
                 *reinterpret_cast<uint2*>(Cb + i * J + j) = pk;
             } else {
-                float* Cf = split_out(blockIdx.y, C, Wsp, I, J);
+                float* Cf = MODE == kScaleRow ? split_out(blockIdx.y, C, Wsp, I, J)
+                                              : reinterpret_cast<float*>(C);
                 *reinterpret_cast<float4*>(Cf + i * J + j) =
                     make_float4(acc[it][jt][0], acc[it][jt][1], acc[it][jt][2], acc[it][jt][3]);
             }
@@ -323,8 +325,9 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
     tile_coords(blockIdx.x, tiles_i, tiles_j, &ti, &tj);
     const int64_t i0 = (int64_t)ti * kBigM, j0 = (int64_t)tj * kBigN;
     const int nkb_all = (int)(Kc / kBK);
-    const int kb0 = split_begin(blockIdx.y, p0, nps);
-    const int nkb = split_end(blockIdx.y, p0, nps, nkb_all) - kb0;
+    // only the row-scaled (wgrad) mode is ever split
+    const int kb0 = MODE == kScaleRow ? split_begin(blockIdx.y, p0, nps) : 0;
+    const int nkb = MODE == kScaleRow ? split_end(blockIdx.y, p0, nps, nkb_all) - kb0 : nkb_all;
     const int64_t jb_count = J / kBN;
 
     // A: rows 32w + 16it + r16 (clamped; rows past I are never stored), the
@@ -500,7 +503,8 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
         } else if constexpr (OUT_BF16) {
             store_bf16(reinterpret_cast<uint16_t*>(C));
         } else {
-            float* Cf = split_out(blockIdx.y, C, Wsp, I, J);
+            float* Cf = MODE == kScaleRow ? split_out(blockIdx.y, C, Wsp, I, J)
+                                          : reinterpret_cast<float*>(C);
 #pragma unroll
             for (int it = 0; it < 2; ++it) {
                 const int64_t i = i0 + 32 * wave + 16 * it + r16;
@@ -582,8 +586,10 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
         // kLagFold: group jp's partials are folded while group jp + 1's MFMAs
         // run, so the FMAs fill the matrix core's issue gaps instead of waiting
         // for the group's last MFMA.  That needs a second set of partials (16
-        // registers), which only the block-scaled instantiations without the
-        // quantizing epilogue have; the others fold each group right after it.
+        // registers).  The quantizing epilogue has no room for them; the
+        // row-scaled mode fits them only by spilling two values outside the
+        // loop and measured no faster with them, so both fold each group
+        // right after it.
         v4f pl[JJ][2];
 #pragma unroll
         for (int jp = 0; jp < 16 / JJ; ++jp) {

@@ -72,84 +72,103 @@ hipError_t launch_quant_rowtile(const uint16_t* x, int64_t M, int64_t K, uint8_t
 }
 
 // ---------------------------------------------------------------------------
-// Weight blocks.  One workgroup per 128x128 block: each thread loads 8 chunks
-// of 8 BF16 (16 threads per 256-byte row), the block amax is reduced across
-// the wave and then across the 4 waves through LDS.  With q_t the codes also
-// go through an LDS tile and leave transposed, 16 bytes per store.
+// Weight blocks.  One workgroup per 128x128 block.  Thread t loads the 16-byte
+// chunk c = t % 16 (8 BF16) of the four consecutive rows 4 (t / 16) + j and,
+// in a second pass, of the rows 64 further on: each load instruction of a wave
+// covers four whole 256-byte rows.  The block amax is reduced across the wave
+// and then across the 4 waves through LDS.  The codes go out row-major as they
+// are (8 bytes per thread and row, whole 128-byte rows per instruction), and,
+// for q_t, each 4 rows x 4 columns of a thread are transposed in registers (4
+// byte permutes per 4 dwords) into four dwords, each holding 4 consecutive
+// rows n of one column k.  Those go to an LDS tile laid out as q_t[k][n] with
+// the 16-byte chunks of row k XOR-swizzled by (k / 8) % 8: a dword store of a
+// wave then touches 32 banks twice at most, and the 16-byte reads that feed
+// the q_t stores (eight lanes per 128-byte row of q_t) are conflict-free.
 // ---------------------------------------------------------------------------
 constexpr int kBlkThreads = 256;
-constexpr int kBlkLdsStride = kTile + 4;   // bytes per code row in LDS
+
+// Dword index in the transposed LDS tile of (k, n/4).
+__device__ __forceinline__ int blk_t_dword(int k, int n4) {
+    return k * 32 + (n4 ^ (((k >> 3) & 7) << 2));
+}
+
+// 4x4 byte transpose: byte j of a_i -> byte i of out[j].
+__device__ __forceinline__ void transpose4x4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
+                                             uint32_t out[4]) {
+    const uint32_t lo01 = __builtin_amdgcn_perm(a1, a0, 0x05010400u);  // a0.b0 a1.b0 a0.b1 a1.b1
+    const uint32_t lo23 = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
+    const uint32_t hi01 = __builtin_amdgcn_perm(a1, a0, 0x07030602u);  // a0.b2 a1.b2 a0.b3 a1.b3
+    const uint32_t hi23 = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
+    out[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+    out[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+    out[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+    out[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+}
 
 __global__ __launch_bounds__(kBlkThreads) void quant_block_kernel(
     const uint16_t* __restrict__ w, int64_t N, int64_t K, uint8_t* __restrict__ q,
     uint8_t* __restrict__ q_t, float* __restrict__ s) {
     __shared__ uint32_t red[kBlkThreads / 64];
-    __shared__ __align__(16) uint8_t codes[kTile * kBlkLdsStride];
+    __shared__ __align__(16) uint32_t tile_t[kTile * kTile / 4];
     __shared__ ScaleTables tab;
     load_scale_tables(&tab);
     const int tid = threadIdx.x;
     const int64_t kb_count = K / kTile;
     const int64_t bi = blockIdx.x / kb_count, bj = blockIdx.x % kb_count;
     const int64_t n0 = bi * kTile, k0 = bj * kTile;
+    const int cc = tid & 15;              // 16-byte chunk of the row: columns 8cc .. 8cc+7
+    const int rg = tid >> 4;              // rows 4rg .. 4rg+3 (+64 in the second pass)
 
-    uint4 v[8];
+    uint4 v[2][4];
     uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        int c = i * kBlkThreads + tid;
-        int row = c >> 4, cc = c & 15;
-        v[i] = load_stream16(w + (n0 + row) * K + k0 + cc * 8);
-        m = absmax_u4(m, v[i]);
-    }
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 64 * h + 4 * rg + j;
+            v[h][j] = load_stream16(w + (n0 + row) * K + k0 + cc * 8);
+            m = absmax_u4(m, v[h][j]);
+        }
     m = absmax_fold(m);
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
     if ((tid & 63) == 0) red[tid >> 6] = m;
     __syncthreads();
     m = max(max(red[0], red[1]), max(red[2], red[3]));
-    TileScale ts = tile_scale(m, &tab);
+    const TileScale ts = tile_scale(m, &tab);
     if (tid == 0) s[bi * kb_count + bj] = ts.s;
 
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        int c = i * kBlkThreads + tid;
-        int row = c >> 4, cc = c & 15;
-        uint2 code = quant8(v[i], ts.inv);
-        *reinterpret_cast<uint2*>(q + (n0 + row) * K + k0 + cc * 8) = code;
+    for (int h = 0; h < 2; ++h) {
+        uint2 code[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 64 * h + 4 * rg + j;
+            code[j] = quant8(v[h][j], ts.inv);
+            *reinterpret_cast<uint2*>(q + (n0 + row) * K + k0 + cc * 8) = code[j];
+        }
         if (q_t) {
-            uint32_t* dst = reinterpret_cast<uint32_t*>(codes + row * kBlkLdsStride + cc * 8);
-            dst[0] = code.x;
-            dst[1] = code.y;
+            const int n4 = 16 * h + rg;   // rows 4 n4 .. 4 n4 + 3
+            uint32_t t0[4], t1[4];
+            transpose4x4(code[0].x, code[1].x, code[2].x, code[3].x, t0);   // columns 8cc .. +3
+            transpose4x4(code[0].y, code[1].y, code[2].y, code[3].y, t1);   // columns 8cc+4 .. +7
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                tile_t[blk_t_dword(8 * cc + kk, n4)] = t0[kk];
+                tile_t[blk_t_dword(8 * cc + 4 + kk, n4)] = t1[kk];
+            }
         }
     }
     if (!q_t) return;
     __syncthreads();
-    // Thread -> 16 (n) x 4 (k) sub-block: read 16 dwords (rows n..n+15, bytes
-    // k..k+3), transpose 4x4 byte groups, write 4 rows of q_t, 16 bytes each.
-    const int nn = (tid & 7) * 16;
-    const int kk = (tid >> 3) * 4;
-    uint32_t d[16];
+    // Row k of q_t's block, 16 rows n per lane: eight lanes per 128-byte row.
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-        d[i] = *reinterpret_cast<const uint32_t*>(codes + (nn + i) * kBlkLdsStride + kk);
-    uint32_t out[4][4];   // out[k'][g] holds n = nn+4g .. nn+4g+3 of row kk+k'
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        uint32_t a0 = d[4 * g + 0], a1 = d[4 * g + 1], a2 = d[4 * g + 2], a3 = d[4 * g + 3];
-        // byte k' of a_i -> byte i of out[k']
-        uint32_t lo01 = __builtin_amdgcn_perm(a1, a0, 0x05010400u);  // a0.b0 a1.b0 a0.b1 a1.b1
-        uint32_t lo23 = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
-        uint32_t hi01 = __builtin_amdgcn_perm(a1, a0, 0x07030602u);  // a0.b2 a1.b2 a0.b3 a1.b3
-        uint32_t hi23 = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
-        out[0][g] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
-        out[1][g] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
-        out[2][g] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
-        out[3][g] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+    for (int p = 0; p < 4; ++p) {
+        const int k = 32 * p + (tid >> 3);
+        const int ch = tid & 7;                        // n = 16 ch .. 16 ch + 15
+        const uint4 d = *reinterpret_cast<const uint4*>(&tile_t[blk_t_dword(k, 4 * ch)]);
+        *reinterpret_cast<uint4*>(q_t + (k0 + k) * N + n0 + 16 * ch) = d;
     }
-#pragma unroll
-    for (int kp = 0; kp < 4; ++kp)
-        *reinterpret_cast<uint4*>(q_t + (k0 + kk + kp) * N + n0 + nn) =
-            make_uint4(out[kp][0], out[kp][1], out[kp][2], out[kp][3]);
 }
 
 hipError_t launch_quant_block(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, uint8_t* q_t,
