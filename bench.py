@@ -143,6 +143,71 @@ def summarize_rocprof(d: str) -> None:
             print("\n".join(ratios))
 
 
+def _pmc_dispatches(d: str, counter: str):
+    """[(kernel name, grid, value)] of one counter, one entry per dispatch,
+    from a rocprofv3 --pmc run (-f csv) under d."""
+    import csv
+    import glob
+    out = {}
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (path, r["Dispatch_Id"])
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            prev = out.get(key, (name, r["Grid_Size"], 0.0))
+            out[key] = (name, r["Grid_Size"], prev[2] + float(r["Counter_Value"]))
+    return list(out.values())
+
+
+def record_traffic(fetch_dir: str, write_dir: str, out_path: str = TRAFFIC_FILE) -> None:
+    """HBM bytes per library call from two counter runs of the step (FETCH_SIZE
+    and WRITE_SIZE, KiB per dispatch, each run made with --copy-calibration-mib
+    1024).  Each counter is scaled by what it reads for that plain 1 GiB
+    device copy; a wgrad call's bytes include its split-K reduction.  Writes
+    the per-kind records (keyed to the kernel sources' digest) and prints the
+    per-kernel lines."""
+    fetch = _pmc_dispatches(fetch_dir, "FETCH_SIZE")
+    write = _pmc_dispatches(write_dir, "WRITE_SIZE")
+    gib_kib = float(1 << 20)
+
+    def factor(rows):
+        copies = [v for n, g, v in rows if "copyBuffer" in n]
+        return gib_kib / max(copies) if copies and max(copies) > 0 else 1.0
+
+    ff, fw = factor(fetch), factor(write)
+    print(f"# scale: the 1 GiB device copy reads {max(v for n, g, v in fetch if 'copyBuffer' in n):.0f} "
+          f"KiB of FETCH_SIZE and {max(v for n, g, v in write if 'copyBuffer' in n):.0f} KiB of "
+          f"WRITE_SIZE; factors applied: FETCH x{ff:.4f}, WRITE x{fw:.4f}")
+    per_kernel = {}
+    for rows, f, col in ((fetch, ff, 0), (write, fw, 1)):
+        for n, g, v in rows:
+            e = per_kernel.setdefault((n, g), [[], []])
+            e[col].append(v * f * 1024)
+    kinds = {}
+    for (n, g), (fb, wb) in sorted(per_kernel.items()):
+        nd = max(len(fb), len(wb))
+        mf = sum(fb) / max(len(fb), 1) / 1e6
+        mw = sum(wb) / max(len(wb), 1) / 1e6
+        print(f"{n[:60]:60s} grid={g:>9s} n={nd:4d} fetch_MB={mf:10.2f} write_MB={mw:10.2f}")
+        kind, is_call = kernel_kind(n)
+        if kind:
+            k = kinds.setdefault(kind, [0.0, 0])
+            k[0] += sum(fb) / max(len(fb), 1) * nd + sum(wb) / max(len(wb), 1) * nd
+            k[1] += nd if is_call else 0
+    rec = {}
+    for kind, (b, calls) in kinds.items():
+        if calls:
+            rec[kind] = {"bytes_per_launch": int(b / calls), "launches": calls,
+                         "profile": "profiles/linear_set_hbm_bytes.txt",
+                         "source_sha256_16": source_digest(kind)}
+    with open(out_path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print("# per library call (a wgrad call includes its split-K reduction)")
+    for kind, r in sorted(rec.items()):
+        print(f"{kind:20s} calls={r['launches']:5d} bytes_per_call={r['bytes_per_launch'] / 1e6:10.2f} MB")
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -164,6 +229,9 @@ def parse():
                          "alone)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-configuration measurements of configurations 1-4")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from a FETCH_SIZE and a WRITE_SIZE "
+                         "rocprofv3 run of the step and print the per-kernel bytes, then exit")
     ap.add_argument("--summarize-rocprof", metavar="DIR",
                     help="print a text summary of rocprofv3 CSV output in DIR and exit")
     return ap.parse_args()
@@ -871,6 +939,9 @@ def main():
     args = parse()
     if args.summarize_rocprof:
         summarize_rocprof(args.summarize_rocprof)
+        return
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the path is "

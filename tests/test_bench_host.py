@@ -2,6 +2,8 @@
 results with the oracle's (fed here with the oracle's own results, then with
 one planted difference each), the kernel-name classification of profiler
 output, and the refusal of more than one GPU."""
+import json
+import os
 import subprocess
 import sys
 
@@ -102,3 +104,31 @@ def test_sclk_parsing_of_both_smi_tools():
 
 def test_cpu_model_is_a_string():
     assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
+
+
+def _pmc_csv(path, counter, rows):
+    import csv
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, "run_counter_collection.csv"), "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Grid_Size", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for i, (name, grid, kib) in enumerate(rows):
+            w.writerow([i, grid, name, counter, kib])
+
+
+def test_traffic_record_scales_by_the_copy_and_groups_calls(tmp_path):
+    copy = ("__amd_rocclr_copyBuffer", "131072")
+    wg = ("fp8bs::gemm_bs_fp8_big_kernel<2, false, false>(unsigned char const*)", "131072")
+    red = ("fp8bs::splitk_reduce_kernel(float const*)", "1048576")
+    # the copy moves 1 GiB = 1048576 KiB; fetch reads half of it, write all of it
+    _pmc_csv(str(tmp_path / "f"), "FETCH_SIZE", [(*copy, 524288), (*wg, 1000), (*red, 300),
+                                                 (*wg, 1200), (*red, 300)])
+    _pmc_csv(str(tmp_path / "w"), "WRITE_SIZE", [(*copy, 1048576), (*wg, 400), (*red, 100),
+                                                 (*wg, 400), (*red, 100)])
+    out = tmp_path / "traffic.json"
+    bench.record_traffic(str(tmp_path / "f"), str(tmp_path / "w"), str(out))
+    rec = json.loads(out.read_text())["gemm_wgrad"]
+    assert rec["launches"] == 2
+    # per call: fetch 2 x (1100 + 300) KiB, write 400 + 100 KiB, in bytes
+    assert rec["bytes_per_launch"] == (2 * (1100 + 300) + (400 + 100)) * 1024
+    assert rec["source_sha256_16"] == bench.source_digest("gemm_wgrad")
