@@ -587,11 +587,39 @@ def parse_sclk_json(text: str):
     return found or None
 
 
+def under_profiler() -> bool:
+    """True inside a rocprofv3 run (its library is preloaded into every
+    process, which then counts as using the GPU)."""
+    return any("rocprof" in os.environ.get(k, "") for k in ("LD_PRELOAD", "HSA_TOOLS_LIB"))
+
+
+def _smi_command(tool: str, args):
+    """argv for an SMI tool.  Both are Python scripts started through
+    /usr/bin/env; running the script with this interpreter avoids env
+    replacing itself with python3 in a child of a process that uses the GPU."""
+    import shutil
+    path = shutil.which(tool) or os.path.join("/opt/rocm/bin", tool)
+    try:
+        with open(path, "rb") as f:
+            first = f.readline()
+    except OSError:
+        return None
+    if first.startswith(b"#!") and b"python" in first:
+        return [sys.executable, path, *args]
+    return [path, *args]
+
+
 def _sclk_from_smi():
     """Current graphics clocks in MHz reported by amd-smi or rocm-smi (a list,
-    one per GPU), or None when neither answers."""
+    one per GPU), or None when neither answers (or under a profiler)."""
     import subprocess
-    for cmd in (["amd-smi", "metric", "--clock", "--json"], ["rocm-smi", "--showclocks", "--json"]):
+    if under_profiler():
+        return None
+    for tool, args in (("amd-smi", ["metric", "--clock", "--json"]),
+                       ("rocm-smi", ["--showclocks", "--json"])):
+        cmd = _smi_command(tool, args)
+        if cmd is None:
+            continue
         try:
             r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
         except (OSError, subprocess.SubprocessError):

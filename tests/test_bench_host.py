@@ -132,3 +132,14 @@ def test_traffic_record_scales_by_the_copy_and_groups_calls(tmp_path):
     # per call: fetch 2 x (1100 + 300) KiB, write 400 + 100 KiB, in bytes
     assert rec["bytes_per_launch"] == (2 * (1100 + 300) + (400 + 100)) * 1024
     assert rec["source_sha256_16"] == bench.source_digest("gemm_wgrad")
+
+
+def test_smi_tools_run_without_an_env_hop(monkeypatch, tmp_path):
+    script = tmp_path / "amd-smi"
+    script.write_text("#!/usr/bin/env python3\nprint('{}')\n")
+    script.chmod(0o755)
+    monkeypatch.setenv("PATH", str(tmp_path) + os.pathsep + os.environ.get("PATH", ""))
+    cmd = bench._smi_command("amd-smi", ["metric"])
+    assert cmd == [sys.executable, str(script), "metric"]
+    monkeypatch.setenv("LD_PRELOAD", "/opt/rocm/lib/librocprofiler-sdk-tool.so")
+    assert bench.under_profiler() and bench._sclk_from_smi() is None
