@@ -325,9 +325,15 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
     tile_coords(blockIdx.x, tiles_i, tiles_j, &ti, &tj);
     const int64_t i0 = (int64_t)ti * kBigM, j0 = (int64_t)tj * kBigN;
     const int nkb_all = (int)(Kc / kBK);
-    // only the row-scaled (wgrad) mode is ever split
-    const int kb0 = MODE == kScaleRow ? split_begin(blockIdx.y, p0, nps) : 0;
-    const int nkb = MODE == kScaleRow ? split_end(blockIdx.y, p0, nps, nkb_all) - kb0 : nkb_all;
+    // Only the row-scaled (wgrad) mode is ever split; the others sum all
+    // blocks.  The quantizing epilogue's instantiation takes its block range
+    // from the launch arguments too (p0 = the block count): the compiler then
+    // waits for a block's A codes once, ahead of the barrier, instead of in
+    // steps among the widenings, and that measured 10% faster for it (and no
+    // faster for the plain instantiations).
+    constexpr bool kRangeArgs = MODE == kScaleRow || QOUT;
+    const int kb0 = kRangeArgs ? split_begin(blockIdx.y, p0, nps) : 0;
+    const int nkb = kRangeArgs ? split_end(blockIdx.y, p0, nps, nkb_all) - kb0 : nkb_all;
     const int64_t jb_count = J / kBN;
 
     // A: rows 32w + 16it + r16 (clamped; rows past I are never stored), the
