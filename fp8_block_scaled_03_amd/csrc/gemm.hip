@@ -17,8 +17,8 @@
 // v_mfma_f32_16x16x32_f16: four chained instructions give P for one 128-wide
 // block in FP32, which is folded into the FP32 accumulator: acc += P * sA*sB,
 // one FMA per output element where sA*sB is one product per row and block
-// (fprop, dgrad), a multiply and an FMA where both scales vary along the
-// tile (wgrad).
+// (fprop, dgrad), a multiply (sA*sB, formed before the MFMAs) and an FMA
+// where both scales vary along the tile (wgrad).
 //
 // Two kernels share that arithmetic:
 //   gemm_bs_fp8_kernel      workgroup tile 128 (i) x 128 (j) x 128 (k), four
@@ -563,6 +563,23 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
 #pragma unroll
             for (int jj = 0; jj < JJ; ++jj) bq[t][jj] = frag(t, jj);
         // Fold one MFMA group's partials (B subtiles JJ jq .. JJ jq + JJ - 1) into acc.
+        // Row-scaled mode: the scale products sA(i) sB(j) of one MFMA group's
+        // outputs, one per element since both scales vary along the tile,
+        // formed before the group's MFMAs.  They do not wait for the MFMA
+        // results, so the multiplies issue while the matrix core works and
+        // only the FMA of the fold waits (3.6% faster over a layer's four
+        // wgrad shapes than multiplying the partials after the MFMAs).
+        v4f csr[JJ][2];
+        auto scale_products = [&](int jq) __attribute__((always_inline)) {
+#pragma unroll
+            for (int jj = 0; jj < JJ; ++jj) {
+                const float4 sb =
+                    *reinterpret_cast<const float4*>(&sBs[buf][16 * (JJ * jq + jj) + 4 * g]);
+#pragma unroll
+                for (int it = 0; it < 2; ++it)
+                    csr[jj][it] = v4f{sa[it] * sb.x, sa[it] * sb.y, sa[it] * sb.z, sa[it] * sb.w};
+            }
+        };
         auto fold = [&](v4f (&q)[JJ][2], int jq) __attribute__((always_inline)) {
 #pragma unroll
             for (int jj = 0; jj < JJ; ++jj) {
@@ -576,16 +593,12 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
                             acc[it][js][v] = __builtin_fmaf(q[jj][it][v], cs, acc[it][js][v]);
                     }
                 } else {
-                    // (P * sB(j)) * sA(i): the column scale is applied in place,
-                    // so the fold needs no registers for scale products.
-                    const float4 sb = *reinterpret_cast<const float4*>(&sBs[buf][16 * js + 4 * g]);
 #pragma unroll
-                    for (int it = 0; it < 2; ++it) {
-                        acc[it][js][0] = __builtin_fmaf(q[jj][it][0] * sb.x, sa[it], acc[it][js][0]);
-                        acc[it][js][1] = __builtin_fmaf(q[jj][it][1] * sb.y, sa[it], acc[it][js][1]);
-                        acc[it][js][2] = __builtin_fmaf(q[jj][it][2] * sb.z, sa[it], acc[it][js][2]);
-                        acc[it][js][3] = __builtin_fmaf(q[jj][it][3] * sb.w, sa[it], acc[it][js][3]);
-                    }
+                    for (int it = 0; it < 2; ++it)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            acc[it][js][v] =
+                                __builtin_fmaf(q[jj][it][v], csr[jj][it][v], acc[it][js][v]);
                 }
             }
         };
@@ -599,6 +612,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
         v4f pl[JJ][2];
 #pragma unroll
         for (int jp = 0; jp < 16 / JJ; ++jp) {
+            if constexpr (MODE == kScaleRow) scale_products(jp);
             v4f p[JJ][2];
 #pragma unroll
             for (int jj = 0; jj < JJ; ++jj)
