@@ -8,7 +8,8 @@ Python functions here carry the C names and only marshal arguments;
 """
 from ._binding import (FP8BS_OUT_BF16, FP8BS_OUT_F32, Fp8bsError, bf16_gemm_tn, capi,  # noqa: F401
                        fp8_encode_e4m3, fp8_gemm_dgrad, fp8_gemm_dgrad_quantized, fp8_gemm_fprop,
-                       fp8_gemm_wgrad, fp8_gemm_wgrad_noalloc,
+                       fp8_gemm_wgrad, fp8_gemm_wgrad_accumulate,
+                       fp8_gemm_wgrad_accumulate_workspace_bytes, fp8_gemm_wgrad_noalloc,
                        fp8_gemm_wgrad_workspace_bytes, fp8_quantize_block,
                        fp8_quantize_dual, fp8_quantize_rowtile, fp8_quantize_transposed,
                        fp8bs_hbm_rate, fp8bs_mfma_rate, fp8bs_status_string, fp8bs_version)

@@ -39,6 +39,9 @@ SIGNATURES = {
     "fp8_gemm_wgrad": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
     "fp8_gemm_wgrad_noalloc": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "fp8_gemm_wgrad_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64]),
+    "fp8_gemm_wgrad_accumulate": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t,
+                                         _P]),
+    "fp8_gemm_wgrad_accumulate_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64]),
     "bf16_gemm_tn": (_INT, [_P, _P, _P, _INT, _I64, _I64, _I64, _P]),
     "fp8_encode_e4m3": (_INT, [_P, _I64, _P, _P]),
     "fp8bs_mfma_rate": (_INT, [_P, _I64, _INT, ctypes.c_float, _P]),
@@ -313,27 +316,60 @@ def _wgrad_operands(dytq, dyts, xtq, xts):
     return M, N, K
 
 
-def fp8_gemm_wgrad(dytq, dyts, xtq, xts, dw=None, workspace=None, stream=None):
-    """dW [N,K] (float32) = dY^T X from (dytq [N,M], dyts [N,M/128]) and (xtq [K,M], xts [K,M/128]).
-    workspace: None (no split), "auto" (allocate the queried size) or a uint8 device tensor."""
-    M, N, K = _wgrad_operands(dytq, dyts, xtq, xts)
+def _workspace_arg(workspace):
+    """True for "auto"; checks a given workspace tensor."""
     auto = isinstance(workspace, str)
     if auto and workspace != "auto":
         raise ValueError(f"workspace: expected None, 'auto' or a tensor, got {workspace!r}")
     if not auto and workspace is not None:
         _need(workspace, torch.uint8, (None,), "workspace")
+    return auto
+
+
+def _auto_workspace(nbytes, device, stream):
+    with _alloc_on(stream, device):
+        return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None
+
+
+def fp8_gemm_wgrad(dytq, dyts, xtq, xts, dw=None, workspace=None, stream=None):
+    """dW [N,K] (float32) = dY^T X from (dytq [N,M], dyts [N,M/128]) and (xtq [K,M], xts [K,M/128]).
+    workspace: None (no split), "auto" (allocate the queried size) or a uint8 device tensor."""
+    M, N, K = _wgrad_operands(dytq, dyts, xtq, xts)
+    auto = _workspace_arg(workspace)
     _on_device(dytq=dytq, dyts=dyts, xtq=xtq, xts=xts)
     dw = _out((N, K), FP8BS_OUT_F32, dytq.device, dw, stream)
     if auto:
-        nbytes = fp8_gemm_wgrad_workspace_bytes(M, N, K)
-        with _alloc_on(stream, dytq.device):
-            workspace = torch.empty(nbytes, dtype=torch.uint8, device=dytq.device) if nbytes else None
+        workspace = _auto_workspace(fp8_gemm_wgrad_workspace_bytes(M, N, K), dytq.device, stream)
     ws_ptr = _ptr(workspace)
     ws_bytes = 0 if workspace is None else workspace.numel()
     _on_device(dytq=dytq, dyts=dyts, xtq=xtq, xts=xts, dw=dw, workspace=workspace)
     _check("fp8_gemm_wgrad", capi().fp8_gemm_wgrad(
         _ptr(dytq), _ptr(dyts), _ptr(xtq), _ptr(xts), _ptr(dw), M, N, K, ws_ptr, ws_bytes,
         _stream(dytq, stream)))
+    return dw
+
+
+def fp8_gemm_wgrad_accumulate_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(capi().fp8_gemm_wgrad_accumulate_workspace_bytes(M, N, K))
+
+
+def fp8_gemm_wgrad_accumulate(dytq, dyts, xtq, xts, dw, workspace=None, stream=None):
+    """dw (float32 [N,K], updated in place) += dY^T X, operands as fp8_gemm_wgrad;
+    the result equals dw + fp8_gemm_wgrad(...) bit for bit.  workspace: None
+    (no split), "auto" or a uint8 device tensor, as fp8_gemm_wgrad (its
+    query is fp8_gemm_wgrad_accumulate_workspace_bytes)."""
+    M, N, K = _wgrad_operands(dytq, dyts, xtq, xts)
+    auto = _workspace_arg(workspace)
+    _need(dw, torch.float32, (N, K), "dw")
+    _on_device(dytq=dytq, dyts=dyts, xtq=xtq, xts=xts, dw=dw)
+    if auto:
+        workspace = _auto_workspace(fp8_gemm_wgrad_accumulate_workspace_bytes(M, N, K),
+                                    dytq.device, stream)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    _on_device(dytq=dytq, dyts=dyts, xtq=xtq, xts=xts, dw=dw, workspace=workspace)
+    _check("fp8_gemm_wgrad_accumulate", capi().fp8_gemm_wgrad_accumulate(
+        _ptr(dytq), _ptr(dyts), _ptr(xtq), _ptr(xts), _ptr(dw), M, N, K, _ptr(workspace),
+        ws_bytes, _stream(dytq, stream)))
     return dw
 
 

@@ -256,6 +256,38 @@ size_t fp8_gemm_wgrad_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     return fp8bs::gemm_workspace_bytes(fp8bs::kScaleRow, N, K, M, cus);
 }
 
+fp8bs_status fp8_gemm_wgrad_accumulate(const uint8_t* dytq, const float* dyts, const uint8_t* xtq,
+                                       const float* xts, float* dw, int64_t M, int64_t N,
+                                       int64_t K, void* workspace, size_t workspace_bytes,
+                                       fp8bs_stream_t stream) {
+    if (!mult128(M) || !mult128(N) || !mult128(K)) return FP8BS_ERR_SHAPE;
+    const bool out_empty = (N == 0 || K == 0);
+    const bool in_empty = out_empty || M == 0;
+    FP8BS_TRY(check_ptr(dytq, in_empty, 16));
+    FP8BS_TRY(check_ptr(dyts, in_empty, 4));
+    FP8BS_TRY(check_ptr(xtq, in_empty, 16));
+    FP8BS_TRY(check_ptr(xts, in_empty, 4));
+    FP8BS_TRY(check_ptr(dw, out_empty, 16));
+    if (workspace && !aligned(workspace, 16)) return FP8BS_ERR_ALIGN;
+    if (out_empty) return FP8BS_OK;
+    int cus;
+    FP8BS_TRY(check_device(&cus));
+    if (workspace && workspace_bytes > 0 &&
+        workspace_bytes < fp8bs::wgrad_accumulate_workspace_bytes(N, K, M, cus))
+        return FP8BS_ERR_WORKSPACE;
+    if (!workspace) workspace_bytes = 0;
+    // TN form, as fp8_gemm_wgrad.
+    return launched(fp8bs::launch_wgrad_accumulate(dytq, dyts, xtq, xts, dw, N, K, M, workspace,
+                                                   workspace_bytes, cus, stream));
+}
+
+size_t fp8_gemm_wgrad_accumulate_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (!mult128(M) || !mult128(N) || !mult128(K)) return 0;
+    int cus = 0;
+    if (check_device(&cus) != FP8BS_OK) return 0;
+    return fp8bs::wgrad_accumulate_workspace_bytes(N, K, M, cus);
+}
+
 fp8bs_status bf16_gemm_tn(const uint16_t* a, const uint16_t* b, void* c, fp8bs_out_dtype ct,
                           int64_t I, int64_t J, int64_t K, fp8bs_stream_t stream) {
     if (I < 0 || !mult128(J) || !mult128(K)) return FP8BS_ERR_SHAPE;

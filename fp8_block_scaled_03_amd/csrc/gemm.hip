@@ -89,7 +89,7 @@ constexpr int kBK = 128;
 constexpr int kThreads = 256;
 constexpr int kTileBytes = kBM * kBK;       // one FP8 operand tile: 16 KB
 
-template <int MODE, bool OUT_BF16>
+template <int MODE, bool OUT_BF16, bool ACC = false>
 __global__ __launch_bounds__(kThreads, 2) void gemm_bs_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
     const float* __restrict__ sB, void* __restrict__ C, int64_t I, int64_t J, int64_t Kc,
@@ -254,8 +254,13 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bs_fp8_kernel(
             } else {
                 float* Cf = MODE == kScaleRow ? split_out(blockIdx.y, C, Wsp, I, J)
                                               : reinterpret_cast<float*>(C);
-                *reinterpret_cast<float4*>(Cf + i * J + j) =
-                    make_float4(acc[it][jt][0], acc[it][jt][1], acc[it][jt][2], acc[it][jt][3]);
+                if constexpr (ACC) {
+                    v4f* dst = reinterpret_cast<v4f*>(Cf + i * J + j);
+                    *dst = *dst + acc[it][jt];
+                } else {
+                    *reinterpret_cast<float4*>(Cf + i * J + j) = make_float4(
+                        acc[it][jt][0], acc[it][jt][1], acc[it][jt][2], acc[it][jt][3]);
+                }
             }
         }
     }
@@ -307,7 +312,7 @@ __device__ __forceinline__ int f16_frag_off(int row, int q) {
     return (((row >> 4) * 4 + (q & 3)) * 64 + (q >> 2) * 16 + (row & 15)) * 16;
 }
 
-template <int MODE, bool OUT_BF16, bool QOUT = false>
+template <int MODE, bool OUT_BF16, bool QOUT = false, bool ACC = false>
 __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
     const float* __restrict__ sB, void* __restrict__ C, int64_t I, int64_t J, int64_t Kc,
@@ -518,8 +523,14 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_bs_fp8_big_kernel(
 #pragma unroll
                 for (int jq = 0; jq < 8; ++jq) {
                     const int js = 8 * h + jq;
-                    *reinterpret_cast<float4*>(Cf + i * J + jh + 16 * jq + 4 * g) =
-                        make_float4(acc[it][js][0], acc[it][js][1], acc[it][js][2], acc[it][js][3]);
+                    if constexpr (ACC) {
+                        v4f* dst = reinterpret_cast<v4f*>(Cf + i * J + jh + 16 * jq + 4 * g);
+                        *dst = *dst + acc[it][js];
+                    } else {
+                        *reinterpret_cast<float4*>(Cf + i * J + jh + 16 * jq + 4 * g) =
+                            make_float4(acc[it][js][0], acc[it][js][1], acc[it][js][2],
+                                        acc[it][js][3]);
+                    }
                 }
             }
         }
@@ -681,7 +692,28 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float4* __rest
     out[e] = a;
 }
 
-template <int MODE, bool BF16>
+// The accumulating form: every piece is in the workspace (piece y in slice
+// y); their sum, in piece order, is added to out once:
+// out[e] = out[e] + (((ws[0][e] + ws[1][e]) + ...)), so the result equals the
+// plain call's result added to out.
+__global__ __launch_bounds__(256) void splitk_reduce_acc_kernel(const float4* __restrict__ ws,
+                                                                float4* __restrict__ out,
+                                                                int64_t n4, int slices) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= n4) return;
+    float4 a = ws[e];
+    for (int s = 1; s < slices; ++s) {
+        const float4 b = ws[(int64_t)s * n4 + e];
+        a.x += b.x;
+        a.y += b.y;
+        a.z += b.z;
+        a.w += b.w;
+    }
+    const float4 o = out[e];
+    out[e] = make_float4(o.x + a.x, o.y + a.y, o.z + a.z, o.w + a.w);
+}
+
+template <int MODE, bool BF16, bool ACC = false>
 static hipError_t launch_small(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB,
                                void* C, int64_t I, int64_t J, int64_t Kc, int pieces, int p0,
                                int nps, float* Wsp, hipStream_t stream) {
@@ -689,17 +721,17 @@ static hipError_t launch_small(const uint8_t* A, const float* sA, const uint8_t*
     int64_t tiles_j = J / kBN;
     int64_t blocks = tiles_i * tiles_j;
     if (blocks == 0) return hipSuccess;
-    return launch(gemm_bs_fp8_kernel<MODE, BF16>, dim3((unsigned)blocks, pieces), dim3(kThreads),
+    return launch(gemm_bs_fp8_kernel<MODE, BF16, ACC>, dim3((unsigned)blocks, pieces), dim3(kThreads),
                   stream, A, sA, B, sB, C, I, J, Kc, (int)tiles_i, (int)tiles_j, p0, nps, Wsp);
 }
 
-template <int MODE, bool BF16>
+template <int MODE, bool BF16, bool ACC = false>
 static hipError_t launch_big(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB,
                              void* C, int64_t I, int64_t J, int64_t Kc, int pieces, int p0,
                              int nps, float* Wsp, hipStream_t stream) {
     int tiles_i = (int)((I + kBigM - 1) / kBigM);
     int tiles_j = (int)((J + kBigN - 1) / kBigN);
-    return launch(gemm_bs_fp8_big_kernel<MODE, BF16>, dim3(tiles_i * tiles_j, pieces),
+    return launch(gemm_bs_fp8_big_kernel<MODE, BF16, false, ACC>, dim3(tiles_i * tiles_j, pieces),
                   dim3(kBigThreads), stream, A, sA, B, sB, C, I, J, Kc, tiles_i, tiles_j, p0, nps,
                   Wsp, (uint8_t*)nullptr, (float*)nullptr);
 }
@@ -846,6 +878,40 @@ static hipError_t launch_mode(const uint8_t* A, const float* sA, const uint8_t* 
     return launch(splitk_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), stream,
                   reinterpret_cast<const float4*>(Wsp), reinterpret_cast<float4*>(C), n4,
                   p.pieces - 1);
+}
+
+size_t wgrad_accumulate_workspace_bytes(int64_t I, int64_t J, int64_t Kc, int num_cus) {
+    const size_t need = gemm_workspace_bytes(kScaleRow, I, J, Kc, num_cus);
+    return need ? need + (size_t)I * (size_t)J * sizeof(float) : 0;
+}
+
+// C += the row-scaled GEMM.  Unsplit, the epilogue adds the result to C.
+// Split, every piece goes to the workspace (piece 0 in slice 0, which is the
+// kernels' output pointer for that launch) and the reduction adds their sum
+// to C; the pieces, the plan and the order of the sum are those of the plain
+// call, so C ends as C + (the plain call's result) bit for bit.
+hipError_t launch_wgrad_accumulate(const uint8_t* A, const float* sA, const uint8_t* B,
+                                   const float* sB, float* C, int64_t I, int64_t J, int64_t Kc,
+                                   void* workspace, size_t workspace_bytes, int num_cus,
+                                   hipStream_t stream) {
+    const size_t need = wgrad_accumulate_workspace_bytes(I, J, Kc, num_cus);
+    const bool can_split = workspace && need > 0 && workspace_bytes >= need;
+    Plan p = plan_gemm(kScaleRow, I, J, Kc, num_cus, can_split);
+    if (p.pieces <= 1)
+        return p.big ? launch_big<kScaleRow, false, true>(A, sA, B, sB, C, I, J, Kc, 1, p.p0, p.nps,
+                                                          nullptr, stream)
+                     : launch_small<kScaleRow, false, true>(A, sA, B, sB, C, I, J, Kc, 1, p.p0,
+                                                            p.nps, nullptr, stream);
+    float* S = reinterpret_cast<float*>(workspace);
+    hipError_t e =
+        p.big ? launch_big<kScaleRow, false>(A, sA, B, sB, S, I, J, Kc, p.pieces, p.p0, p.nps,
+                                             S + I * J, stream)
+              : launch_small<kScaleRow, false>(A, sA, B, sB, S, I, J, Kc, p.pieces, p.p0, p.nps,
+                                               S + I * J, stream);
+    if (e != hipSuccess) return e;
+    const int64_t n4 = I * J / 4;
+    return launch(splitk_reduce_acc_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), stream,
+                  reinterpret_cast<const float4*>(S), reinterpret_cast<float4*>(C), n4, p.pieces);
 }
 
 hipError_t launch_gemm_quantized(ScaleMode mode, const uint8_t* A, const float* sA,

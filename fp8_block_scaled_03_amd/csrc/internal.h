@@ -53,6 +53,15 @@ hipError_t launch_gemm(ScaleMode mode, const uint8_t* A, const float* sA, const 
 
 size_t gemm_workspace_bytes(ScaleMode mode, int64_t I, int64_t J, int64_t Kc, int num_cus);
 
+// C[I, J] += the kScaleRow launch_gemm result (FP32), C holding FP32 values on
+// entry.  The split plan needs wgrad_accumulate_workspace_bytes (every piece,
+// the first included, in the workspace); with less, the call does not split.
+size_t wgrad_accumulate_workspace_bytes(int64_t I, int64_t J, int64_t Kc, int num_cus);
+hipError_t launch_wgrad_accumulate(const uint8_t* A, const float* sA, const uint8_t* B,
+                                   const float* sB, float* C, int64_t I, int64_t J, int64_t Kc,
+                                   void* workspace, size_t workspace_bytes, int num_cus,
+                                   hipStream_t stream);
+
 // As launch_gemm with BF16 output (C, nullable), plus the output quantized in
 // 1x128 row tiles: codes Cq [I, J], scales Cs [I, J/128].  Modes kScaleBlock
 // and kScaleBlockT; 256x256 kernel, no split.

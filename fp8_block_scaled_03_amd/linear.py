@@ -14,8 +14,9 @@ or FP32.  This module is that usage for one layer, over the C ABI only:
             dW = fp8_gemm_wgrad (FP32).
 
 dW is returned in FP32 (autograd casts it to the parameter's dtype), or, when
-the weight carries an FP32 ``main_grad`` tensor, added into that tensor and
-not returned, the usual home of weight gradients in mixed-precision training.
+the weight carries an FP32 ``main_grad`` tensor, added into that tensor by the
+wgrad GEMM itself (fp8_gemm_wgrad_accumulate) and not returned, the usual home
+of weight gradients in mixed-precision training.
 T (the flattened token count), ``in`` and ``out`` must be multiples of 128.
 There is no fallback: without the HIP library every call raises.
 """
@@ -62,13 +63,17 @@ class Fp8LinearFunction(torch.autograd.Function):
         if ctx.needs_input_grad[0]:
             dx = B.fp8_gemm_dgrad(dyq, dys, wqt, ws, out_dtype=torch.bfloat16)
         if ctx.needs_input_grad[1]:
-            ws_arg = ctx.workspace if ctx.workspace is not None else "auto"
-            dw32 = B.fp8_gemm_wgrad(dytq, dyts, xtq, xts, workspace=ws_arg)
             main = getattr(ctx.weight, "main_grad", None)
+            ws_arg = ctx.workspace if ctx.workspace is not None else "auto"
             if main is not None:
-                main.add_(dw32)
+                # Summed into main_grad by the GEMM itself (no separate pass).
+                need = B.fp8_gemm_wgrad_accumulate_workspace_bytes(
+                    xtq.shape[1], dytq.shape[0], xtq.shape[0])
+                if ctx.workspace is not None and ctx.workspace.numel() < need:
+                    ws_arg = "auto"
+                B.fp8_gemm_wgrad_accumulate(dytq, dyts, xtq, xts, main, workspace=ws_arg)
             else:
-                dw = dw32
+                dw = B.fp8_gemm_wgrad(dytq, dyts, xtq, xts, workspace=ws_arg)
         return dx, dw, None
 
 
@@ -77,8 +82,10 @@ class Fp8Linear(torch.nn.Module):
     forward and backward matmuls run through the FP8 block-scaled kernels.
 
     ``workspace``: optional uint8 device tensor for the wgrad split-K slices
-    (at least ``fp8_gemm_wgrad_workspace_bytes`` of the layer's shape); when
-    None, each backward allocates what the library asks for.
+    (at least ``fp8_gemm_wgrad_workspace_bytes`` of the layer's shape, or
+    ``fp8_gemm_wgrad_accumulate_workspace_bytes`` when the weight carries a
+    ``main_grad``); when None or smaller, each backward allocates what the
+    library asks for.
     """
 
     def __init__(self, in_features: int, out_features: int, device=None, std: float = 0.02,

@@ -198,6 +198,36 @@ fp8bs_status fp8_gemm_wgrad_noalloc(const uint8_t* dytq, const float* dyts, cons
 size_t fp8_gemm_wgrad_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
+ * wgrad accumulated into an existing FP32 gradient: dw[n][k] += G[n][k],
+ * where G is the dW fp8_gemm_wgrad computes for the same operands (Puro-2B
+ * report, section 2 "FP8": weight gradients and other training state stay in
+ * FP32 beside the FP8 matmuls, so a layer's weight gradient is summed into a
+ * held FP32 gradient buffer; this does the sum in the same call instead of a
+ * separate pass over dW).
+ *   dytq, dyts, xtq, xts, M, N, K: as fp8_gemm_wgrad (caller-owned).
+ *   dw f32 [N, K]: read and written (caller-owned, FP32 values on entry).
+ * The result is dw + G with G summed first, rounded once per element, so it
+ * equals dw + (fp8_gemm_wgrad's result) bit for bit.  M == 0 adds zeros.
+ * workspace: optional device scratch (see
+ * fp8_gemm_wgrad_accumulate_workspace_bytes: it holds every piece of the
+ * split, the first included).  With workspace == NULL, workspace_bytes == 0
+ * or a shape that does not split, the call does not split and the GEMM's
+ * epilogue adds into dw; a non-NULL workspace smaller than the query returns
+ * FP8BS_ERR_WORKSPACE.  The split result is deterministic run to run.
+ * Errors and alignment as fp8_gemm_wgrad.
+ */
+fp8bs_status fp8_gemm_wgrad_accumulate(const uint8_t* dytq, const float* dyts, const uint8_t* xtq,
+                                       const float* xts, float* dw, int64_t M, int64_t N,
+                                       int64_t K, void* workspace, size_t workspace_bytes,
+                                       fp8bs_stream_t stream);
+
+/* Bytes of workspace fp8_gemm_wgrad_accumulate uses for this shape on the
+ * current device (16-byte aligned): fp8_gemm_wgrad_workspace_bytes plus one
+ * N x K FP32 slice when the shape splits, else 0.  Negative or invalid shapes
+ * give 0. */
+size_t fp8_gemm_wgrad_accumulate_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
  * dgrad with its output quantized as it is produced (the row-tile quantizer
  * fused into the GEMM epilogue; Puro-2B technical report, section 2 "FP8":
  * BF16 work next to the FP8 matmuls then needs no separate pass over dX to

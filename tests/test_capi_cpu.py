@@ -39,7 +39,7 @@ def L():
 
 def test_exports_every_header_symbol(L):
     names = header_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -127,6 +127,19 @@ def test_gemm_argument_errors(L):
     assert n(None, None, None, None, None, 128, 0, 128, None) == OK
     assert L.fp8_gemm_wgrad_workspace_bytes(100, 128, 128) == 0
     assert L.fp8_gemm_wgrad_workspace_bytes(-128, 128, 128) == 0
+
+    a = L.fp8_gemm_wgrad_accumulate
+    assert a(A16, A16, A16, A16, A16, 100, 128, 128, None, 0, None) == SHAPE
+    assert a(A16, A16, A16, A16, A16, 128, 128, 96, None, 0, None) == SHAPE
+    assert a(A16, A16, A16, A16, A16, -128, 128, 128, None, 0, None) == SHAPE
+    assert a(A16, A16, None, A16, A16, 128, 128, 128, None, 0, None) == NULL
+    assert a(A16, A16, A16, A16, None, 128, 128, 128, None, 0, None) == NULL
+    assert a(A16, A16 + 2, A16, A16, A16, 128, 128, 128, None, 0, None) == ALIGN
+    assert a(A16, A16, A16, A16, A16 + 8, 128, 128, 128, None, 0, None) == ALIGN
+    assert a(A16, A16, A16, A16, A16, 128, 128, 128, MIS, 64, None) == ALIGN
+    assert a(None, None, None, None, None, 128, 128, 0, None, 0, None) == OK
+    assert L.fp8_gemm_wgrad_accumulate_workspace_bytes(128, 100, 128) == 0
+    assert L.fp8_gemm_wgrad_accumulate_workspace_bytes(128, 128, -128) == 0
 
 
 def test_dgrad_quantized_argument_errors(L):
@@ -238,6 +251,14 @@ def test_binding_rejects_mismatched_inputs_before_any_call(monkeypatch):
         ("output", lambda: B.fp8_gemm_fprop(xq, xs, wq, ws, y=E((256, 64), bf))),
         ("workspace", lambda: B.fp8_gemm_wgrad(xq, xs, E((128, 256), u8), E((128, 2), f32),
                                                workspace=E((64,), f32))),
+        ("dw", lambda: B.fp8_gemm_wgrad_accumulate(xq, xs, E((128, 256), u8), E((128, 2), f32),
+                                                   E((256, 64), f32))),
+        ("dw", lambda: B.fp8_gemm_wgrad_accumulate(xq, xs, E((128, 256), u8), E((128, 2), f32),
+                                                   E((256, 128), bf))),
+        ("xts", lambda: B.fp8_gemm_wgrad_accumulate(xq, xs, E((128, 256), u8), E((128, 1), f32),
+                                                    E((256, 128), f32))),
+        ("workspace", lambda: B.fp8_gemm_wgrad_accumulate(
+            xq, xs, E((128, 256), u8), E((128, 2), f32), E((256, 128), f32), workspace="big")),
     ]
     for what, call in cases:
         with pytest.raises(ValueError, match=what):
