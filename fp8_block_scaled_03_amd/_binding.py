@@ -35,6 +35,10 @@ SIGNATURES = {
     "fp8_quantize_dual": (_INT, [_P, _I64, _I64, _P, _P, _P, _P, _P]),
     "fp8_gemm_fprop": (_INT, [_P, _P, _P, _P, _P, _INT, _I64, _I64, _I64, _P]),
     "fp8_gemm_dgrad": (_INT, [_P, _P, _P, _P, _P, _INT, _I64, _I64, _I64, _P]),
+    "fp8_gemm_fprop_mfma8": (_INT, [_P, _P, _P, _P, _P, _INT, _I64, _I64, _I64, _P]),
+    "fp8_gemm_dgrad_mfma8": (_INT, [_P, _P, _P, _P, _P, _INT, _I64, _I64, _I64, _P]),
+    "fp8_gemm_wgrad_mfma8": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
+    "fp8_gemm_wgrad_mfma8_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64]),
     "fp8_gemm_dgrad_quantized": (_INT, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "fp8_gemm_wgrad": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
     "fp8_gemm_wgrad_noalloc": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
@@ -249,8 +253,7 @@ def _row_operand(q, s, what):
     return R, L
 
 
-def fp8_gemm_fprop(xq, xs, wq, ws, out_dtype=torch.bfloat16, y=None, stream=None):
-    """Y [M,N] = X W^T from (xq [M,K], xs [M,K/128]) and (wq [N,K], ws [N/128,K/128])."""
+def _fprop(name, xq, xs, wq, ws, out_dtype, y, stream):
     M, K = _row_operand(xq, xs, "xq")
     N, _ = _dims(wq, "wq")
     _need(wq, torch.uint8, (N, K), "wq")
@@ -258,9 +261,20 @@ def fp8_gemm_fprop(xq, xs, wq, ws, out_dtype=torch.bfloat16, y=None, stream=None
     code = _dtype_code(out_dtype)
     y = _out((M, N), code, xq.device, y, stream)
     _on_device(xq=xq, xs=xs, wq=wq, ws=ws, y=y)
-    _check("fp8_gemm_fprop", capi().fp8_gemm_fprop(
+    _check(name, getattr(capi(), name)(
         _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(y), code, M, N, K, _stream(xq, stream)))
     return y
+
+
+def fp8_gemm_fprop(xq, xs, wq, ws, out_dtype=torch.bfloat16, y=None, stream=None):
+    """Y [M,N] = X W^T from (xq [M,K], xs [M,K/128]) and (wq [N,K], ws [N/128,K/128])."""
+    return _fprop("fp8_gemm_fprop", xq, xs, wq, ws, out_dtype, y, stream)
+
+
+def fp8_gemm_fprop_mfma8(xq, xs, wq, ws, out_dtype=torch.bfloat16, y=None, stream=None):
+    """fp8_gemm_fprop with each block's sum formed by the FP8 MFMA (limited
+    precision inside the block, see include/fp8bs.h)."""
+    return _fprop("fp8_gemm_fprop_mfma8", xq, xs, wq, ws, out_dtype, y, stream)
 
 
 def _dgrad_operands(dyq, dys, wq_t, ws):
@@ -271,15 +285,24 @@ def _dgrad_operands(dyq, dys, wq_t, ws):
     return M, N, K
 
 
-def fp8_gemm_dgrad(dyq, dys, wq_t, ws, out_dtype=torch.bfloat16, dx=None, stream=None):
-    """dX [M,K] = dY W from (dyq [M,N], dys [M,N/128]) and (wq_t [K,N], ws [N/128,K/128])."""
+def _dgrad(name, dyq, dys, wq_t, ws, out_dtype, dx, stream):
     M, N, K = _dgrad_operands(dyq, dys, wq_t, ws)
     code = _dtype_code(out_dtype)
     dx = _out((M, K), code, dyq.device, dx, stream)
     _on_device(dyq=dyq, dys=dys, wq_t=wq_t, ws=ws, dx=dx)
-    _check("fp8_gemm_dgrad", capi().fp8_gemm_dgrad(
+    _check(name, getattr(capi(), name)(
         _ptr(dyq), _ptr(dys), _ptr(wq_t), _ptr(ws), _ptr(dx), code, M, N, K, _stream(dyq, stream)))
     return dx
+
+
+def fp8_gemm_dgrad(dyq, dys, wq_t, ws, out_dtype=torch.bfloat16, dx=None, stream=None):
+    """dX [M,K] = dY W from (dyq [M,N], dys [M,N/128]) and (wq_t [K,N], ws [N/128,K/128])."""
+    return _dgrad("fp8_gemm_dgrad", dyq, dys, wq_t, ws, out_dtype, dx, stream)
+
+
+def fp8_gemm_dgrad_mfma8(dyq, dys, wq_t, ws, out_dtype=torch.bfloat16, dx=None, stream=None):
+    """fp8_gemm_dgrad with each block's sum formed by the FP8 MFMA."""
+    return _dgrad("fp8_gemm_dgrad_mfma8", dyq, dys, wq_t, ws, out_dtype, dx, stream)
 
 
 def fp8_gemm_dgrad_quantized(dyq, dys, wq_t, ws, with_bf16=True, dx=None, dxq=None, dxs=None,
@@ -331,22 +354,37 @@ def _auto_workspace(nbytes, device, stream):
         return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None
 
 
-def fp8_gemm_wgrad(dytq, dyts, xtq, xts, dw=None, workspace=None, stream=None):
-    """dW [N,K] (float32) = dY^T X from (dytq [N,M], dyts [N,M/128]) and (xtq [K,M], xts [K,M/128]).
-    workspace: None (no split), "auto" (allocate the queried size) or a uint8 device tensor."""
+def _wgrad(name, dytq, dyts, xtq, xts, dw, workspace, stream):
     M, N, K = _wgrad_operands(dytq, dyts, xtq, xts)
     auto = _workspace_arg(workspace)
     _on_device(dytq=dytq, dyts=dyts, xtq=xtq, xts=xts)
     dw = _out((N, K), FP8BS_OUT_F32, dytq.device, dw, stream)
     if auto:
-        workspace = _auto_workspace(fp8_gemm_wgrad_workspace_bytes(M, N, K), dytq.device, stream)
+        nbytes = int(getattr(capi(), name + "_workspace_bytes")(M, N, K))
+        workspace = _auto_workspace(nbytes, dytq.device, stream)
     ws_ptr = _ptr(workspace)
     ws_bytes = 0 if workspace is None else workspace.numel()
     _on_device(dytq=dytq, dyts=dyts, xtq=xtq, xts=xts, dw=dw, workspace=workspace)
-    _check("fp8_gemm_wgrad", capi().fp8_gemm_wgrad(
+    _check(name, getattr(capi(), name)(
         _ptr(dytq), _ptr(dyts), _ptr(xtq), _ptr(xts), _ptr(dw), M, N, K, ws_ptr, ws_bytes,
         _stream(dytq, stream)))
     return dw
+
+
+def fp8_gemm_wgrad(dytq, dyts, xtq, xts, dw=None, workspace=None, stream=None):
+    """dW [N,K] (float32) = dY^T X from (dytq [N,M], dyts [N,M/128]) and (xtq [K,M], xts [K,M/128]).
+    workspace: None (no split), "auto" (allocate the queried size) or a uint8 device tensor."""
+    return _wgrad("fp8_gemm_wgrad", dytq, dyts, xtq, xts, dw, workspace, stream)
+
+
+def fp8_gemm_wgrad_mfma8_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(capi().fp8_gemm_wgrad_mfma8_workspace_bytes(M, N, K))
+
+
+def fp8_gemm_wgrad_mfma8(dytq, dyts, xtq, xts, dw=None, workspace=None, stream=None):
+    """fp8_gemm_wgrad with each block's sum formed by the FP8 MFMA; workspace
+    as fp8_gemm_wgrad (its query is fp8_gemm_wgrad_mfma8_workspace_bytes)."""
+    return _wgrad("fp8_gemm_wgrad_mfma8", dytq, dyts, xtq, xts, dw, workspace, stream)
 
 
 def fp8_gemm_wgrad_accumulate_workspace_bytes(M: int, N: int, K: int) -> int:

@@ -160,7 +160,7 @@ fp8bs_status fp8_quantize_dual(const uint16_t* x, int64_t M, int64_t C, uint8_t*
 static fp8bs_status gemm_common(fp8bs::ScaleMode mode, const uint8_t* A, const float* sA,
                                 const uint8_t* B, const float* sB, void* C, int yt, int64_t I,
                                 int64_t J, int64_t Kc, void* workspace, size_t workspace_bytes,
-                                fp8bs_stream_t stream) {
+                                fp8bs_stream_t stream, bool mfma8 = false) {
     if (yt != FP8BS_OUT_F32 && yt != FP8BS_OUT_BF16) return FP8BS_ERR_DTYPE;
     const bool out_empty = (I == 0 || J == 0);
     const bool in_empty = out_empty || Kc == 0;
@@ -173,10 +173,13 @@ static fp8bs_status gemm_common(fp8bs::ScaleMode mode, const uint8_t* A, const f
     if (out_empty) return FP8BS_OK;
     int cus;
     FP8BS_TRY(check_device(&cus));
-    if (workspace && workspace_bytes > 0 &&
-        workspace_bytes < fp8bs::gemm_workspace_bytes(mode, I, J, Kc, cus))
-        return FP8BS_ERR_WORKSPACE;
+    const size_t need = mfma8 ? fp8bs::gemm_mfma8_workspace_bytes(mode, I, J, Kc, cus)
+                              : fp8bs::gemm_workspace_bytes(mode, I, J, Kc, cus);
+    if (workspace && workspace_bytes > 0 && workspace_bytes < need) return FP8BS_ERR_WORKSPACE;
     if (!workspace) workspace_bytes = 0;
+    if (mfma8)
+        return launched(fp8bs::launch_gemm_mfma8(mode, A, sA, B, sB, C, yt == FP8BS_OUT_BF16, I,
+                                                 J, Kc, workspace, workspace_bytes, cus, stream));
     return launched(fp8bs::launch_gemm(mode, A, sA, B, sB, C, yt == FP8BS_OUT_BF16, I, J, Kc,
                                        workspace, workspace_bytes, cus, stream));
 }
@@ -196,6 +199,37 @@ fp8bs_status fp8_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t*
     // TN form: rows of dY (contraction N) against rows of W^T ([K, N]).
     return gemm_common(fp8bs::kScaleBlockT, dyq, dys, wq_t, ws, dx, enum_value(dxt), M, K, N,
                        nullptr, 0, stream);
+}
+
+fp8bs_status fp8_gemm_fprop_mfma8(const uint8_t* xq, const float* xs, const uint8_t* wq,
+                                  const float* ws, void* y, fp8bs_out_dtype yt, int64_t M,
+                                  int64_t N, int64_t K, fp8bs_stream_t stream) {
+    if (M < 0 || !mult128(N) || !mult128(K)) return FP8BS_ERR_SHAPE;
+    return gemm_common(fp8bs::kScaleBlock, xq, xs, wq, ws, y, enum_value(yt), M, N, K, nullptr, 0,
+                       stream, true);
+}
+
+fp8bs_status fp8_gemm_dgrad_mfma8(const uint8_t* dyq, const float* dys, const uint8_t* wq_t,
+                                  const float* ws, void* dx, fp8bs_out_dtype dxt, int64_t M,
+                                  int64_t N, int64_t K, fp8bs_stream_t stream) {
+    if (M < 0 || !mult128(N) || !mult128(K)) return FP8BS_ERR_SHAPE;
+    return gemm_common(fp8bs::kScaleBlockT, dyq, dys, wq_t, ws, dx, enum_value(dxt), M, K, N,
+                       nullptr, 0, stream, true);
+}
+
+fp8bs_status fp8_gemm_wgrad_mfma8(const uint8_t* dytq, const float* dyts, const uint8_t* xtq,
+                                  const float* xts, float* dw, int64_t M, int64_t N, int64_t K,
+                                  void* workspace, size_t workspace_bytes, fp8bs_stream_t stream) {
+    if (!mult128(M) || !mult128(N) || !mult128(K)) return FP8BS_ERR_SHAPE;
+    return gemm_common(fp8bs::kScaleRow, dytq, dyts, xtq, xts, dw, FP8BS_OUT_F32, N, K, M,
+                       workspace, workspace_bytes, stream, true);
+}
+
+size_t fp8_gemm_wgrad_mfma8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (!mult128(M) || !mult128(N) || !mult128(K)) return 0;
+    int cus = 0;
+    if (check_device(&cus) != FP8BS_OK) return 0;
+    return fp8bs::gemm_mfma8_workspace_bytes(fp8bs::kScaleRow, N, K, M, cus);
 }
 
 fp8bs_status fp8_gemm_dgrad_quantized(const uint8_t* dyq, const float* dys, const uint8_t* wq_t,

@@ -68,21 +68,6 @@ __device__ __forceinline__ v8h widen8(uint32_t lo, uint32_t hi) {
     return v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// Contraction split of a FP32-output GEMM: piece 0 sums blocks [0, p0) and
-// writes the output itself; piece y >= 1 sums blocks [p0 + (y-1) nps,
-// p0 + y nps) (the last one clipped to the contraction) into FP32 slice y-1
-// of the workspace Wsp.  splitk_reduce_kernel then adds the slices to the
-// output in piece order.  An unsplit launch has p0 = the block count.
-__device__ __forceinline__ int split_begin(int y, int p0, int nps) {
-    return y == 0 ? 0 : p0 + (y - 1) * nps;
-}
-__device__ __forceinline__ int split_end(int y, int p0, int nps, int nkb_all) {
-    return min(nkb_all, y == 0 ? p0 : p0 + y * nps);
-}
-__device__ __forceinline__ float* split_out(int y, void* C, float* Wsp, int64_t I, int64_t J) {
-    return y == 0 ? reinterpret_cast<float*>(C) : Wsp + (int64_t)(y - 1) * I * J;
-}
-
 constexpr int kBM = 128;
 constexpr int kBN = 128;
 constexpr int kBK = 128;
@@ -830,9 +815,9 @@ static Plan plan_gemm_uncached(ScaleMode mode, int64_t I, int64_t J, int64_t Kc,
 // Plans depend only on the shape, the device's CU count and the options, so
 // each is simulated once per process.
 static Plan plan_gemm(ScaleMode mode, int64_t I, int64_t J, int64_t Kc, int num_cus,
-                      bool allow_split) {
+                      bool allow_split, int force = -1) {
     const int cus = num_cus > 0 ? num_cus : 256;
-    const int force = kernel_override();
+    if (force < 0) force = kernel_override();
     static std::mutex mu;
     static std::map<std::tuple<int, int64_t, int64_t, int64_t, int, bool, int>, Plan> cache;
     const auto key = std::make_tuple((int)mode, I, J, Kc, cus, allow_split, force);
@@ -846,6 +831,21 @@ static Plan plan_gemm(ScaleMode mode, int64_t I, int64_t J, int64_t Kc, int num_
     if (cache.size() > 4096) cache.clear();
     cache.emplace(key, p);
     return p;
+}
+
+hipError_t launch_splitk_reduce(const float* ws, float* out, int64_t n, int slices,
+                               hipStream_t stream) {
+    const int64_t n4 = n / 4;
+    if (n4 == 0 || slices <= 0) return hipSuccess;
+    return launch(splitk_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), stream,
+                  reinterpret_cast<const float4*>(ws), reinterpret_cast<float4*>(out), n4,
+                  slices);
+}
+
+GemmSplit big_tile_split(ScaleMode mode, int64_t I, int64_t J, int64_t Kc, int num_cus,
+                         bool allow_split) {
+    const Plan p = plan_gemm(mode, I, J, Kc, num_cus, allow_split, 2);
+    return GemmSplit{p.pieces, p.p0, p.nps};
 }
 
 size_t gemm_workspace_bytes(ScaleMode mode, int64_t I, int64_t J, int64_t Kc, int num_cus) {

@@ -44,4 +44,19 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_i, int tiles_j, i
     *tj = r / rows;
 }
 
+// Contraction split of a FP32-output GEMM: piece 0 sums blocks [0, p0) and
+// writes the output itself; piece y >= 1 sums blocks [p0 + (y-1) nps,
+// p0 + y nps) (the last one clipped to the contraction) into FP32 slice y-1
+// of the workspace Wsp.  splitk_reduce_kernel then adds the slices to the
+// output in piece order.  An unsplit launch has p0 = the block count.
+__device__ __forceinline__ int split_begin(int y, int p0, int nps) {
+    return y == 0 ? 0 : p0 + (y - 1) * nps;
+}
+__device__ __forceinline__ int split_end(int y, int p0, int nps, int nkb_all) {
+    return min(nkb_all, y == 0 ? p0 : p0 + y * nps);
+}
+__device__ __forceinline__ float* split_out(int y, void* C, float* Wsp, int64_t I, int64_t J) {
+    return y == 0 ? reinterpret_cast<float*>(C) : Wsp + (int64_t)(y - 1) * I * J;
+}
+
 }  // namespace fp8bs

@@ -53,6 +53,32 @@ hipError_t launch_gemm(ScaleMode mode, const uint8_t* A, const float* sA, const 
 
 size_t gemm_workspace_bytes(ScaleMode mode, int64_t I, int64_t J, int64_t Kc, int num_cus);
 
+// Contraction split of the 256x256-tile kernels for this shape: `pieces`
+// launches along grid y, piece 0 over blocks [0, p0), the others nps blocks
+// each (split_begin / split_end); pieces == 1 when allow_split is false or a
+// split does not pay.
+struct GemmSplit {
+    int pieces;
+    int p0;
+    int nps;
+};
+GemmSplit big_tile_split(ScaleMode mode, int64_t I, int64_t J, int64_t Kc, int num_cus,
+                         bool allow_split);
+// out[e] = ((out[e] + ws[0][e]) + ws[1][e]) + ..., `slices` FP32 slices of n
+// elements (n a multiple of 4) after out.
+hipError_t launch_splitk_reduce(const float* ws, float* out, int64_t n, int slices,
+                               hipStream_t stream);
+
+// As launch_gemm, with each block's sum P formed by gfx950's FP8 MFMA
+// (v_mfma_f32_16x16x128_f8f6f4) instead of exactly: always the 256x256 tile;
+// a row-scaled (kScaleRow, FP32) launch splits when workspace_bytes covers
+// gemm_mfma8_workspace_bytes.
+size_t gemm_mfma8_workspace_bytes(ScaleMode mode, int64_t I, int64_t J, int64_t Kc, int num_cus);
+hipError_t launch_gemm_mfma8(ScaleMode mode, const uint8_t* A, const float* sA, const uint8_t* B,
+                             const float* sB, void* C, bool out_bf16, int64_t I, int64_t J,
+                             int64_t Kc, void* workspace, size_t workspace_bytes, int num_cus,
+                             hipStream_t stream);
+
 // C[I, J] += the kScaleRow launch_gemm result (FP32), C holding FP32 values on
 // entry.  The split plan needs wgrad_accumulate_workspace_bytes (every piece,
 // the first included, in the workspace); with less, the call does not split.

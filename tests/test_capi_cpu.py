@@ -39,7 +39,7 @@ def L():
 
 def test_exports_every_header_symbol(L):
     names = header_functions()
-    assert len(names) == 18, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -127,6 +127,21 @@ def test_gemm_argument_errors(L):
     assert n(None, None, None, None, None, 128, 0, 128, None) == OK
     assert L.fp8_gemm_wgrad_workspace_bytes(100, 128, 128) == 0
     assert L.fp8_gemm_wgrad_workspace_bytes(-128, 128, 128) == 0
+
+    for f in (L.fp8_gemm_fprop_mfma8, L.fp8_gemm_dgrad_mfma8):
+        assert f(A16, A16, A16, A16, A16, 0, 4, 100, 128, None) == SHAPE
+        assert f(A16, A16, A16, A16, A16, 0, -4, 128, 128, None) == SHAPE
+        assert f(A16, A16, A16, A16, A16, 7, 4, 128, 128, None) == DTYPE
+        assert f(None, A16, A16, A16, A16, 0, 4, 128, 128, None) == NULL
+        assert f(A16, A16, MIS, A16, A16, 0, 4, 128, 128, None) == ALIGN
+        assert f(A16, A16, A16, A16, A16 + 8, 1, 4, 128, 128, None) == ALIGN
+        assert f(None, None, None, None, None, 0, 0, 128, 128, None) == OK
+    m = L.fp8_gemm_wgrad_mfma8
+    assert m(A16, A16, A16, A16, A16, 100, 128, 128, None, 0, None) == SHAPE
+    assert m(A16, A16, A16, A16, None, 128, 128, 128, None, 0, None) == NULL
+    assert m(A16, A16, A16, A16, A16, 128, 128, 128, MIS, 64, None) == ALIGN
+    assert m(None, None, None, None, None, 128, 0, 128, None, 0, None) == OK
+    assert L.fp8_gemm_wgrad_mfma8_workspace_bytes(128, 100, 128) == 0
 
     a = L.fp8_gemm_wgrad_accumulate
     assert a(A16, A16, A16, A16, A16, 100, 128, 128, None, 0, None) == SHAPE
@@ -251,6 +266,9 @@ def test_binding_rejects_mismatched_inputs_before_any_call(monkeypatch):
         ("output", lambda: B.fp8_gemm_fprop(xq, xs, wq, ws, y=E((256, 64), bf))),
         ("workspace", lambda: B.fp8_gemm_wgrad(xq, xs, E((128, 256), u8), E((128, 2), f32),
                                                workspace=E((64,), f32))),
+        ("wq", lambda: B.fp8_gemm_fprop_mfma8(xq, xs, E((128, 128), u8), ws)),
+        ("wq_t", lambda: B.fp8_gemm_dgrad_mfma8(xq, xs, E((128, 128), u8), ws)),
+        ("xts", lambda: B.fp8_gemm_wgrad_mfma8(xq, xs, E((128, 256), u8), E((128, 1), f32))),
         ("dw", lambda: B.fp8_gemm_wgrad_accumulate(xq, xs, E((128, 256), u8), E((128, 2), f32),
                                                    E((256, 64), f32))),
         ("dw", lambda: B.fp8_gemm_wgrad_accumulate(xq, xs, E((128, 256), u8), E((128, 2), f32),
