@@ -67,6 +67,9 @@ def kernel_kind(name: str):
     m = re.search(r"gemm_bs_fp8(?:_big)?_kernel<(\d)", name)
     if m:
         return ("gemm_fprop", "gemm_dgrad", "gemm_wgrad")[int(m.group(1))], True
+    m = re.search(r"gemm_mfma8_kernel<(\d)", name)
+    if m:
+        return ("gemm_fprop_mfma8", "gemm_dgrad_mfma8", "gemm_wgrad_mfma8")[int(m.group(1))], True
     if "quant_dual_kernel<false>" in name:          # the token-axis-only instance
         return "quant_transposed", True
     for k in ("quant_rowtile", "quant_block", "quant_transposed", "quant_dual"):
@@ -102,13 +105,30 @@ def summarize_rocprof(d: str) -> None:
             print(f"{name:64s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
                   f"{float(r['TotalDurationNs']) / 1e6:10.3f} {float(r['Percentage']):6.2f}")
         per_kind = {}
-        for r in csv.DictReader(open(path)):
-            kind, is_call = kernel_kind(r["Name"])
-            if kind:
-                k = per_kind.setdefault(kind, [0.0, 0])
-                k[0] += float(r["TotalDurationNs"])
-                k[1] += int(r["Calls"]) if is_call else 0
-        print("# per library call (split-K reductions counted with their wgrad call)")
+        trace = os.path.join(os.path.dirname(path), os.path.basename(path).replace(
+            "kernel_stats.csv", "kernel_trace.csv"))
+        if os.path.exists(trace):
+            # dispatch order: a split-K reduction belongs to the wgrad call before it
+            last_wgrad = "gemm_wgrad"
+            rows = sorted(csv.DictReader(open(trace)), key=lambda r: int(r["Dispatch_Id"]))
+            for r in rows:
+                kind, is_call = kernel_kind(r["Kernel_Name"])
+                if kind and kind.startswith("gemm_wgrad") and is_call:
+                    last_wgrad = kind
+                elif kind and not is_call:
+                    kind = last_wgrad
+                if kind:
+                    k = per_kind.setdefault(kind, [0.0, 0])
+                    k[0] += float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+                    k[1] += 1 if is_call else 0
+        else:
+            for r in csv.DictReader(open(path)):
+                kind, is_call = kernel_kind(r["Name"])
+                if kind:
+                    k = per_kind.setdefault(kind, [0.0, 0])
+                    k[0] += float(r["TotalDurationNs"])
+                    k[1] += int(r["Calls"]) if is_call else 0
+        print("# per library call (split-K reductions counted with the wgrad call they follow)")
         print(f"{'kind':20s} {'calls':>6s} {'avg_us_per_call':>16s} {'total_ms':>10s}")
         for kind, (ns, calls) in sorted(per_kind.items(), key=lambda kv: -kv[1][0]):
             print(f"{kind:20s} {calls:6d} {ns / max(calls, 1) / 1e3:16.2f} {ns / 1e6:10.3f}")
