@@ -101,7 +101,7 @@ def summarize_rocprof(d: str) -> None:
         print(f"# {os.path.relpath(path, d)}")
         print(f"{'kernel':64s} {'calls':>6s} {'avg_us':>10s} {'total_ms':>10s} {'pct':>6s}")
         for r in csv.DictReader(open(path)):
-            name = r["Name"].split("(")[0].replace("void ", "")[:64]
+            name = r["Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")[:64]
             print(f"{name:64s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
                   f"{float(r['TotalDurationNs']) / 1e6:10.3f} {float(r['Percentage']):6.2f}")
         per_kind = {}
@@ -136,7 +136,7 @@ def summarize_rocprof(d: str) -> None:
     for path in pmc:
         agg = {}
         for r in csv.DictReader(open(path)):
-            name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
             key = (name, r["Grid_Size"])
             a = agg.setdefault(key, {"dispatches": set()})
             a["dispatches"].add(r["Dispatch_Id"])
@@ -174,7 +174,7 @@ def _pmc_dispatches(d: str, counter: str):
             if r["Counter_Name"] != counter:
                 continue
             key = (path, r["Dispatch_Id"])
-            name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
             prev = out.get(key, (name, r["Grid_Size"], 0.0))
             out[key] = (name, r["Grid_Size"], prev[2] + float(r["Counter_Value"]))
     return list(out.values())
