@@ -1017,6 +1017,14 @@ def fp8_linear_comparison(torch, fp8, reps=5):
             m.weight.grad = None
             m(x).backward(dy)
 
+    def fp8_mfma8_layer():
+        for m, x, dy in zip(mods, xs, dys):
+            x.grad = None
+            m.weight.grad = None
+            m.mfma8 = True
+            m(x).backward(dy)
+            m.mfma8 = False
+
     def bf16_layer():
         for w, x, dy in zip(bf_w, xs, dys):
             x.grad = None
@@ -1025,6 +1033,7 @@ def fp8_linear_comparison(torch, fp8, reps=5):
 
     flops = sum(3 * 2 * T * d_in * d_out for _, d_in, d_out in LAYER_LINEARS)
     ms8 = _time_events(torch, fp8_layer, reps)
+    ms8m = _time_events(torch, fp8_mfma8_layer, reps)
     ms16 = _time_events(torch, bf16_layer, reps)
     return {"f4_fp8_linear_layer": {
         "workload": "one decoder layer's QKV, O, gate/up and down linears at 16384 tokens, "
@@ -1032,7 +1041,9 @@ def fp8_linear_comparison(torch, fp8, reps=5):
                     "W, fprop, dgrad, wgrad)",
         "fp8_ms": round(ms8, 3), "fp8_tflops": round(flops / ms8 / 1e9, 1),
         "torch_bf16_ms": round(ms16, 3), "torch_bf16_tflops": round(flops / ms16 / 1e9, 1),
-        "fp8_speedup_vs_torch_bf16": round(ms16 / ms8, 3)}}
+        "fp8_speedup_vs_torch_bf16": round(ms16 / ms8, 3),
+        "fp8_mfma8_ms": round(ms8m, 3), "fp8_mfma8_tflops": round(flops / ms8m / 1e9, 1),
+        "fp8_mfma8_speedup_vs_torch_bf16": round(ms16 / ms8m, 3)}}
 
 
 def mfma8_step(torch, plan, stream, fused, args, exact_value, layer0_fn):

@@ -40,7 +40,7 @@ class Fp8LinearFunction(torch.autograd.Function):
     """y = x @ w.T with FP8 block-scaled forward and backward matmuls."""
 
     @staticmethod
-    def forward(ctx, x2d: torch.Tensor, weight: torch.Tensor, workspace):
+    def forward(ctx, x2d: torch.Tensor, weight: torch.Tensor, workspace, mfma8: bool = False):
         if x2d.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
             raise ValueError("Fp8Linear works on bfloat16 inputs and weights")
         x2d = x2d.contiguous()
@@ -48,10 +48,12 @@ class Fp8LinearFunction(torch.autograd.Function):
         _check_dims(x2d.shape[0], x2d.shape[1], w.shape[0])
         xq, xs, xtq, xts = B.fp8_quantize_dual(x2d)
         wq, wqt, ws = B.fp8_quantize_block(w, with_transpose=True)
-        y = B.fp8_gemm_fprop(xq, xs, wq, ws, out_dtype=torch.bfloat16)
+        fprop = B.fp8_gemm_fprop_mfma8 if mfma8 else B.fp8_gemm_fprop
+        y = fprop(xq, xs, wq, ws, out_dtype=torch.bfloat16)
         ctx.save_for_backward(xtq, xts, wqt, ws)
         ctx.weight = weight
         ctx.workspace = workspace
+        ctx.mfma8 = mfma8
         return y
 
     @staticmethod
@@ -61,11 +63,22 @@ class Fp8LinearFunction(torch.autograd.Function):
         dyq, dys, dytq, dyts = B.fp8_quantize_dual(dy)
         dx = dw = None
         if ctx.needs_input_grad[0]:
-            dx = B.fp8_gemm_dgrad(dyq, dys, wqt, ws, out_dtype=torch.bfloat16)
+            dgrad = B.fp8_gemm_dgrad_mfma8 if ctx.mfma8 else B.fp8_gemm_dgrad
+            dx = dgrad(dyq, dys, wqt, ws, out_dtype=torch.bfloat16)
         if ctx.needs_input_grad[1]:
             main = getattr(ctx.weight, "main_grad", None)
             ws_arg = ctx.workspace if ctx.workspace is not None else "auto"
-            if main is not None:
+            if ctx.mfma8:
+                need = B.fp8_gemm_wgrad_mfma8_workspace_bytes(
+                    xtq.shape[1], dytq.shape[0], xtq.shape[0])
+                if ctx.workspace is not None and ctx.workspace.numel() < need:
+                    ws_arg = "auto"
+                dw32 = B.fp8_gemm_wgrad_mfma8(dytq, dyts, xtq, xts, workspace=ws_arg)
+                if main is not None:
+                    main.add_(dw32)      # this mode has no fused accumulation
+                else:
+                    dw = dw32
+            elif main is not None:
                 # Summed into main_grad by the GEMM itself (no separate pass).
                 need = B.fp8_gemm_wgrad_accumulate_workspace_bytes(
                     xtq.shape[1], dytq.shape[0], xtq.shape[0])
@@ -74,7 +87,7 @@ class Fp8LinearFunction(torch.autograd.Function):
                 B.fp8_gemm_wgrad_accumulate(dytq, dyts, xtq, xts, main, workspace=ws_arg)
             else:
                 dw = B.fp8_gemm_wgrad(dytq, dyts, xtq, xts, workspace=ws_arg)
-        return dx, dw, None
+        return dx, dw, None, None
 
 
 class Fp8Linear(torch.nn.Module):
@@ -86,10 +99,14 @@ class Fp8Linear(torch.nn.Module):
     ``fp8_gemm_wgrad_accumulate_workspace_bytes`` when the weight carries a
     ``main_grad``); when None or smaller, each backward allocates what the
     library asks for.
+
+    ``mfma8``: run the three GEMMs as fp8_gemm_*_mfma8, whose block sums come
+    from the FP8 matrix core (its limited accumulation precision inside each
+    128-wide block, at twice the FP16 rate) instead of exactly.
     """
 
     def __init__(self, in_features: int, out_features: int, device=None, std: float = 0.02,
-                 workspace: torch.Tensor | None = None):
+                 workspace: torch.Tensor | None = None, mfma8: bool = False):
         super().__init__()
         _check_dims(128, in_features, out_features)
         self.in_features = in_features
@@ -98,12 +115,14 @@ class Fp8Linear(torch.nn.Module):
             torch.empty(out_features, in_features, device=device, dtype=torch.bfloat16))
         torch.nn.init.normal_(self.weight, std=std)
         self.workspace = workspace
+        self.mfma8 = mfma8
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         lead = x.shape[:-1]
         y = Fp8LinearFunction.apply(x.reshape(math.prod(lead), self.in_features), self.weight,
-                                    self.workspace)
+                                    self.workspace, self.mfma8)
         return y.reshape(*lead, self.out_features)
 
     def extra_repr(self) -> str:
-        return f"in_features={self.in_features}, out_features={self.out_features}, fp8=block-scaled"
+        mode = "block-scaled, FP8-MFMA block sums" if self.mfma8 else "block-scaled"
+        return f"in_features={self.in_features}, out_features={self.out_features}, fp8={mode}"

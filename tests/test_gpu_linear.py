@@ -99,3 +99,34 @@ def test_fp8_linear_close_to_bf16_matmul():
     ref = x.float() @ lin.weight.float().T
     rel = (torch.linalg.norm(y - ref) / torch.linalg.norm(ref)).item()
     assert 5e-3 < rel < 6e-2, rel
+
+
+def test_fp8_linear_mfma8_runs_the_mfma8_gemms():
+    """Fp8Linear(mfma8=True): Y, dX and dW equal, bit for bit, the
+    fp8_gemm_*_mfma8 calls on the layer's own quantizations, and meet those
+    calls' accumulation bound against the oracle."""
+    from test_gpu_mfma8 import check_mfma8
+    T, d_in, d_out = 384, 256, 640
+    xb = inputs.random_bits((46, T, d_in), (T, d_in), "normal")
+    wb = inputs.normal((47, d_out, d_in), (d_out, d_in), 0.02)
+    dyb = inputs.student_t((48, T, d_out), (T, d_out), 3.0, 1e-3)
+    lin = fp8.Fp8Linear(d_in, d_out, device="cuda", mfma8=True)
+    with torch.no_grad():
+        lin.weight.copy_(to_dev_bf16(wb))
+    lin.weight.main_grad = torch.zeros(d_out, d_in, dtype=torch.float32, device="cuda")
+    x = to_dev_bf16(xb).requires_grad_(True)
+    y = lin(x)
+    y.backward(to_dev_bf16(dyb))
+    xq, xs, xtq, xts = fp8.fp8_quantize_dual(to_dev_bf16(xb))
+    wq, wqt, ws = fp8.fp8_quantize_block(to_dev_bf16(wb))
+    dyq, dys, dytq, dyts = fp8.fp8_quantize_dual(to_dev_bf16(dyb))
+    y8 = fp8.fp8_gemm_fprop_mfma8(xq, xs, wq, ws)
+    dx8 = fp8.fp8_gemm_dgrad_mfma8(dyq, dys, wqt, ws)
+    dw8 = fp8.fp8_gemm_wgrad_mfma8(dytq, dyts, xtq, xts, workspace="auto")
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(y), to_np(y8))
+    assert np.array_equal(to_np(x.grad), to_np(dx8))
+    assert np.array_equal(to_np(lin.weight.main_grad).view(np.uint32), to_np(dw8).view(np.uint32))
+    ry, rdx, rdw, deq = _oracle_layer(xb, wb, dyb)
+    check_mfma8(to_np(lin.weight.main_grad), rdw, deq["dyt"], deq["xt"], "Fp8Linear(mfma8) dW")
+    check_mfma8(to_np(y), ry, deq["x"], deq["w"], "Fp8Linear(mfma8) Y", bf16=True)
