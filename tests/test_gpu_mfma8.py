@@ -165,3 +165,25 @@ def test_mfma8_full_size_sampled_rows():
     ref = oracle.gemm_fprop(oq, os_, owq, ows)
     check_mfma8(got, ref, oracle.dequantize_rows(oq, os_), oracle.dequantize_block(owq, ows),
                 f"qkv fprop_mfma8 {g.M}x{g.N}x{g.K}, {len(rows)} rows")
+
+
+def test_mfma8_empty_contraction_writes_zeros():
+    """K = 0 (fprop, dgrad) and M = 0 (wgrad): every output element is 0."""
+    M, N = 300, 384
+    e8 = lambda r: torch.empty((r, 0), dtype=torch.uint8, device="cuda")
+    es = lambda r: torch.empty((r, 0), dtype=torch.float32, device="cuda")
+    y = torch.full((M, N), 7.0, dtype=torch.float32, device="cuda")
+    fp8.fp8_gemm_fprop_mfma8(e8(M), es(M), e8(N), torch.empty((N // 128, 0), dtype=torch.float32,
+                                                             device="cuda"), out_dtype="f32", y=y)
+    dw = torch.full((N, 256), 7.0, dtype=torch.float32, device="cuda")
+    fp8.fp8_gemm_wgrad_mfma8(e8(N), es(N), e8(256), es(256), dw=dw)
+    torch.cuda.synchronize()
+    assert not y.any() and not dw.any()
+
+
+def test_mfma8_is_deterministic():
+    ops, _, _, _ = _fprop_case(512, 768, 1024, 98)
+    a = fp8.fp8_gemm_fprop_mfma8(*ops, out_dtype="f32")
+    b = fp8.fp8_gemm_fprop_mfma8(*ops, out_dtype="f32")
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
