@@ -128,16 +128,13 @@ __global__ __launch_bounds__(kT8Threads, 1) void gemm_mfma8_kernel(
     const int bh = lane >> 5;
     const int64_t bj = min(j0 + brow, J - 1);
     const uint8_t* b_src = B + bj * Kc + 64 * bh;
-    const float* sbr_src = MODE == kScaleRow ? sB + bj * nkb_all : sB;
     const int64_t jb0 = j0 / 128;
     const int64_t jb1 = min(jb0 + 1, jb_count - 1);
-    uint4 bn[4];              // next block's B codes
-    float sbrn = 0.f;
+    uint4 bn[4];              // next block's B codes (block-scaled modes)
     auto load_b = [&](int kb) __attribute__((always_inline)) {
         const int64_t koff = (int64_t)kb * 128;
 #pragma unroll
         for (int q = 0; q < 4; ++q) bn[q] = *reinterpret_cast<const uint4*>(b_src + koff + 16 * q);
-        if (MODE == kScaleRow) sbrn = sbr_src[kb];
     };
     // The opaque register dependence (an asm statement stays between the LDS
     // reads around it) keeps the compiler from hoisting these stores, and
@@ -150,7 +147,6 @@ __global__ __launch_bounds__(kT8Threads, 1) void gemm_mfma8_kernel(
             asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
             *reinterpret_cast<uint4*>(&Bs[buf][lds_off(brow, 4 * bh + q)]) = w;
         }
-        if (MODE == kScaleRow && bh == 0) sBs[buf][brow] = sbrn;
     };
     uint4 an[2][2];           // next block's A codes
     float san[2], sbn0 = 0.f, sbn1 = 0.f;
