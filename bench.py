@@ -997,6 +997,43 @@ def dgrad_epilogue_quantization(torch, fp8, cfg, reps=5):
         "fused_speedup": round(sep / fused, 3)}}
 
 
+def swiglu_quantization(torch, fp8, reps=5):
+    """The MLP's SwiGLU at 16,384 tokens (gate/up [16384, 12288] -> H [16384,
+    6144]) followed by both quantizations of H that the down projection needs:
+    torch's BF16 SwiGLU then fp8_quantize_dual, against
+    fp8_swiglu_quantize_dual (H never stored, or stored as well)."""
+    T, F = 16384, 6144
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    gu = torch.randn(T, 2 * F, device="cuda", generator=gen).bfloat16()
+    q = torch.empty(T, F, device="cuda", dtype=torch.uint8)
+    s = torch.empty(T, F // 128, device="cuda", dtype=torch.float32)
+    qt = torch.empty(F, T, device="cuda", dtype=torch.uint8)
+    st = torch.empty(F, T // 128, device="cuda", dtype=torch.float32)
+    h = torch.empty(T, F, device="cuda", dtype=torch.bfloat16)
+
+    def separate():
+        torch.mul(torch.nn.functional.silu(gu[:, :F]), gu[:, F:], out=h)
+        fp8.fp8_quantize_dual(h, q, s, qt, st)
+
+    sep = _time_events(torch, separate, reps)
+    fused = _time_events(torch, lambda: fp8.fp8_swiglu_quantize_dual(gu, q, s, qt, st), reps)
+    fused_h = _time_events(torch, lambda: fp8.fp8_swiglu_quantize_dual(gu, q, s, qt, st, h=h),
+                           reps)
+    # read gate and up (4 B per element of H), write both code sets (2 B) and both
+    # scale sets (2 x 4 B per 128 elements)
+    algo = T * F * (4 + 2 + 8 / 128)
+    rate = algo / (fused * 1e-3) / 1e9
+    del gu, q, s, qt, st, h
+    torch.cuda.empty_cache()
+    return {"f3_swiglu_quantize_on_produce": {
+        "workload": "the MLP's SwiGLU at 16384 tokens (gate/up [16384, 12288] bf16 -> H "
+                    "[16384, 6144]) with H's row-tile and token-axis quantization",
+        "separate_ms": round(sep, 4), "fused_ms": round(fused, 4),
+        "fused_with_bf16_h_ms": round(fused_h, 4), "fused_speedup": round(sep / fused, 3),
+        "fused_algorithmic_bytes": int(algo), "fused_gbs": round(rate, 1),
+        "fused_frac_hbm": round(rate / PEAK_HBM_GBS, 4)}}
+
+
 def fp8_linear_comparison(torch, fp8, reps=5):
     """One decoder layer's four linears at 16,384 tokens, forward + backward:
     through Fp8Linear (the FP8 block-scaled path) and through torch's BF16
@@ -1253,6 +1290,7 @@ def main():
                           if k.startswith("gemm")) / cfg_layers
         result["next_rows"] = {**bf16_comparison(torch, fp8, cfg_obj, fp8_gemm_ms, mfma8_gemm_ms),
                                **dgrad_epilogue_quantization(torch, fp8, cfg_obj),
+                               **swiglu_quantization(torch, fp8),
                                **fp8_linear_comparison(torch, fp8)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity_sample"], parity8 = cpu_baseline(

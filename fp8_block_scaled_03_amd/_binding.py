@@ -33,6 +33,7 @@ SIGNATURES = {
     "fp8_quantize_block": (_INT, [_P, _I64, _I64, _P, _P, _P, _P]),
     "fp8_quantize_transposed": (_INT, [_P, _I64, _I64, _P, _P, _P]),
     "fp8_quantize_dual": (_INT, [_P, _I64, _I64, _P, _P, _P, _P, _P]),
+    "fp8_swiglu_quantize_dual": (_INT, [_P, _I64, _I64, _P, _P, _P, _P, _P, _P]),
     "fp8_gemm_fprop": (_INT, [_P, _P, _P, _P, _P, _INT, _I64, _I64, _I64, _P]),
     "fp8_gemm_dgrad": (_INT, [_P, _P, _P, _P, _P, _INT, _I64, _I64, _I64, _P]),
     "fp8_gemm_fprop_mfma8": (_INT, [_P, _P, _P, _P, _P, _INT, _I64, _I64, _I64, _P]),
@@ -225,6 +226,37 @@ def fp8_quantize_dual(x: torch.Tensor, q=None, s=None, qt=None, st=None, stream=
     _check("fp8_quantize_dual", capi().fp8_quantize_dual(
         _ptr(x), M, C, _ptr(q), _ptr(s), _ptr(qt), _ptr(st), _stream(x, stream)))
     return q, s, qt, st
+
+
+def fp8_swiglu_quantize_dual(gate_up: torch.Tensor, q=None, s=None, qt=None, st=None, h=None,
+                             with_h: bool = False, stream=None):
+    """gate_up bf16 [M,2F] (gate | up) -> H = silu(gate) * up quantized on
+    produce: (q [M,F], s [M,F/128], qt [F,M], st [F,M/128], h bf16 [M,F] or None).
+    H is returned (and written) only with with_h=True or a given h."""
+    M, F2 = _dims(gate_up, "gate_up")
+    _need(gate_up, torch.bfloat16, (M, F2), "gate_up")
+    if F2 % 2:
+        raise ValueError(f"gate_up: expected an even number of columns, got {F2}")
+    F = F2 // 2
+    dev = gate_up.device
+    with _alloc_on(stream, dev):
+        q = torch.empty((M, F), dtype=torch.uint8, device=dev) if q is None else q
+        s = torch.empty((M, F // 128), dtype=torch.float32, device=dev) if s is None else s
+        qt = torch.empty((F, M), dtype=torch.uint8, device=dev) if qt is None else qt
+        st = torch.empty((F, M // 128), dtype=torch.float32, device=dev) if st is None else st
+        if with_h and h is None:
+            h = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
+    _need(q, torch.uint8, (M, F), "q")
+    _need(s, torch.float32, (M, _blocks(F)), "s")
+    _need(qt, torch.uint8, (F, M), "qt")
+    _need(st, torch.float32, (F, _blocks(M)), "st")
+    if h is not None:
+        _need(h, torch.bfloat16, (M, F), "h")
+    _on_device(gate_up=gate_up, q=q, s=s, qt=qt, st=st, h=h)
+    _check("fp8_swiglu_quantize_dual", capi().fp8_swiglu_quantize_dual(
+        _ptr(gate_up), M, F, _ptr(q), _ptr(s), _ptr(qt), _ptr(st), _ptr(h),
+        _stream(gate_up, stream)))
+    return q, s, qt, st, h
 
 
 # ----------------------------------------------------------------------- GEMMs

@@ -203,10 +203,47 @@ constexpr int kDualStrideDw = 72;                    // dwords per LDS token row
 
 __device__ __forceinline__ int dual_row(int r) { return ((r & 15) << 3) + (r >> 4); }
 
-template <bool ROWS>
-__global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
-    const uint16_t* __restrict__ x, int64_t M, int64_t C, uint8_t* __restrict__ q,
-    float* __restrict__ s, uint8_t* __restrict__ qt, float* __restrict__ st) {
+// Where a thread's BF16 values come from: 8 consecutive channels (col ..
+// col+7) of token row `row`.  DualPlain reads them from X [M, C].
+struct DualPlain {
+    const uint16_t* __restrict__ x;
+    int64_t C;
+    __device__ __forceinline__ uint4 operator()(int64_t row, int64_t col) const {
+        return load_stream16(x + row * C + col);
+    }
+};
+
+// SwiGLU of the MLP, formed on the way in: h = silu(g) * u, silu(g) =
+// g / (1 + e^-g), in FP32 and rounded to BF16 (ties to even), with the gate g
+// in columns 0..F-1 of the gate/up projection's output [M, 2F] and the up
+// value u in columns F..2F-1.  The exponential and the reciprocal are the
+// hardware approximations (relative error near 2^-20 for the gates of real
+// activations), far inside BF16's 2^-9 rounding step.  H itself is stored
+// only when h is given.
+__device__ __forceinline__ float swiglu_f32(float g, float u) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+struct DualSwiglu {
+    const uint16_t* __restrict__ gu;
+    int64_t F;
+    uint16_t* __restrict__ h;
+    __device__ __forceinline__ uint4 operator()(int64_t row, int64_t col) const {
+        const uint16_t* p = gu + row * 2 * F + col;
+        const uint4 g = load_stream16(p), u = load_stream16(p + F);
+        uint4 r;
+        r.x = pack_bf16x2(swiglu_f32(bf16_lo(g.x), bf16_lo(u.x)), swiglu_f32(bf16_hi(g.x), bf16_hi(u.x)));
+        r.y = pack_bf16x2(swiglu_f32(bf16_lo(g.y), bf16_lo(u.y)), swiglu_f32(bf16_hi(g.y), bf16_hi(u.y)));
+        r.z = pack_bf16x2(swiglu_f32(bf16_lo(g.z), bf16_lo(u.z)), swiglu_f32(bf16_hi(g.z), bf16_hi(u.z)));
+        r.w = pack_bf16x2(swiglu_f32(bf16_lo(g.w), bf16_lo(u.w)), swiglu_f32(bf16_hi(g.w), bf16_hi(u.w)));
+        if (h) *reinterpret_cast<uint4*>(h + row * F + col) = r;
+        return r;
+    }
+};
+
+template <bool ROWS, class Src>
+__device__ __forceinline__ void dual_tile(const Src& src, int64_t M, int64_t C,
+                                          uint8_t* __restrict__ q, float* __restrict__ s,
+                                          uint8_t* __restrict__ qt, float* __restrict__ st) {
     __shared__ __align__(16) uint32_t tile[kTile * kDualStrideDw];
     __shared__ ScaleTables tab;
     load_scale_tables(&tab);
@@ -220,7 +257,7 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
     uint4 v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        v[i] = load_stream16(x + (m0 + 32 * i + rsub) * C + c0 + chunk * 8);
+        v[i] = src(m0 + 32 * i + rsub, c0 + chunk * 8);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 32 * i + rsub;
@@ -283,6 +320,28 @@ __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
             st[(ch + 1) * mbn + mb] = t1.s;
         }
     }
+}
+
+template <bool ROWS>
+__global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t C, uint8_t* __restrict__ q,
+    float* __restrict__ s, uint8_t* __restrict__ qt, float* __restrict__ st) {
+    dual_tile<ROWS>(DualPlain{x, C}, M, C, q, s, qt, st);
+}
+
+__global__ __launch_bounds__(kDualThreads) void swiglu_dual_kernel(
+    const uint16_t* __restrict__ gu, int64_t M, int64_t F, uint8_t* __restrict__ q,
+    float* __restrict__ s, uint8_t* __restrict__ qt, float* __restrict__ st,
+    uint16_t* __restrict__ h) {
+    dual_tile<true>(DualSwiglu{gu, F, h}, M, F, q, s, qt, st);
+}
+
+hipError_t launch_swiglu_dual(const uint16_t* gu, int64_t M, int64_t F, uint8_t* q, float* s,
+                              uint8_t* qt, float* st, uint16_t* h, hipStream_t stream) {
+    int64_t blocks = (M / kTile) * (F / kTile);
+    if (blocks == 0) return hipSuccess;
+    return launch(swiglu_dual_kernel, dim3((unsigned)blocks), dim3(kDualThreads), stream, gu, M, F,
+                  q, s, qt, st, h);
 }
 
 hipError_t launch_quant_transposed(const uint16_t* x, int64_t M, int64_t C, uint8_t* qt, float* st,

@@ -127,6 +127,29 @@ fp8bs_status fp8_quantize_dual(const uint16_t* x, int64_t M, int64_t C, uint8_t*
                                uint8_t* qt, float* st, fp8bs_stream_t stream);
 
 /*
+ * SwiGLU with its output quantized on produce (Puro-2B report, section 2
+ * "FP8": only the main linear matmuls run in FP8; elementwise work such as the
+ * MLP's SwiGLU stays in BF16/FP32).  H = silu(G) * U is formed in FP32 and
+ * rounded to BF16, exactly where a separate SwiGLU kernel would round it, and
+ * that BF16 H is quantized as fp8_quantize_dual(H) would quantize it: the
+ * down projection's two operands (row tiles for its fprop, token-axis tiles
+ * for its wgrad) come out of one read of the gate/up output, and H is never
+ * written to memory in BF16 unless h is given.
+ *   gate_up bf16 [M, 2F]  G = columns 0 .. F-1, U = columns F .. 2F-1
+ *   q   u8   [M, F],  s  f32 [M, F/128]      row tiles of H
+ *   qt  u8   [F, M],  st f32 [F, M/128]      token-axis tiles of H
+ *   h   bf16 [M, F] or NULL                  H itself, when given
+ * silu(g) = g / (1 + e^-g), evaluated with the hardware exponential and
+ * reciprocal (relative error about 2^-20 at the gate values of real
+ * activations), so H is within one BF16 unit of the exactly rounded value and
+ * the codes are those of fp8_quantize_dual applied to the H this call forms.
+ * M, F >= 0 and multiples of 128.  Inputs must be finite.
+ */
+fp8bs_status fp8_swiglu_quantize_dual(const uint16_t* gate_up, int64_t M, int64_t F, uint8_t* q,
+                                      float* s, uint8_t* qt, float* st, uint16_t* h,
+                                      fp8bs_stream_t stream);
+
+/*
  * fprop GEMM: Y = X W^T (Puro-2B report, section 2 "FP8": the forward matmul
  * of a main linear layer in FP8).
  *   xq  u8  [M, K],  xs f32 [M, K/128]          from fp8_quantize_rowtile(X)

@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_quantize_transposed.argtypes = [P, i64, i64, P, P, ctypes.c_int]
         L.oracle_gemm.restype = ctypes.c_int
         L.oracle_gemm.argtypes = [ctypes.c_int, P, P, P, P, i64, i64, i64, P, i64, P, ctypes.c_int]
+        L.oracle_swiglu_bf16.restype = ctypes.c_int
+        L.oracle_swiglu_bf16.argtypes = [P, i64, i64, P, ctypes.c_int]
         L.oracle_gemm_bf16.restype = ctypes.c_int
         L.oracle_gemm_bf16.argtypes = [P, P, i64, i64, i64, P, i64, P, ctypes.c_int]
         L.oracle_version.restype = ctypes.c_int
@@ -167,6 +169,20 @@ def quantize_transposed(x: np.ndarray, threads: int = 0):
     _check(lib().oracle_quantize_transposed(_ptr(x), M, C, _ptr(qt), _ptr(st), threads),
            "transposed")
     return qt, st
+
+
+# ------------------------------------------------------------------ SwiGLU
+def swiglu(gu: np.ndarray, threads: int = 0) -> np.ndarray:
+    """gate/up bf16 bits [M, 2F] -> H = silu(gate) * up, bf16 bits [M, F]
+    (gate = the first F columns, up = the last F; exact in double, one
+    rounding to BF16)."""
+    gu = _u16(gu)
+    M, F2 = gu.shape
+    if F2 % 2:
+        raise ValueError("gate/up input needs an even number of columns")
+    h = np.empty((M, F2 // 2), dtype=np.uint16)
+    _check(lib().oracle_swiglu_bf16(_ptr(gu), M, F2 // 2, _ptr(h), threads), "swiglu")
+    return h
 
 
 # ------------------------------------------------------------------------- GEMMs

@@ -330,6 +330,53 @@ int oracle_gemm(int mode, const uint8_t* A, const float* sA, const uint8_t* B, c
 }
 
 /* ------------------------------------------------------------------------- */
+/* SwiGLU, the BF16 elementwise op of the MLP that produces the input H of     */
+/* the down projection (the report keeps such numerically sensitive work in   */
+/* BF16/FP32 and runs only the main linear matmuls in FP8):                   */
+/*     h[m][f] = silu(g) * u,   silu(g) = g / (1 + e^(-g)),                     */
+/* with the gate g = gu[m][f] (the first F columns of the gate/up projection's */
+/* output [M, 2F]) and the up value u = gu[m][F + f] (the last F).  Evaluated */
+/* in double (exp from libm) and rounded once to BF16, ties to even.          */
+/* ------------------------------------------------------------------------- */
+/* double -> BF16 bits with one rounding, to nearest, ties to even: a normal   */
+/* BF16 value has 8 significant bits, so the rounding unit of |v| in           */
+/* [2^(e-1), 2^e) is 2^(e-8); below 2^-126 the unit is fixed at 2^-133 (BF16   */
+/* subnormals).  A result of 2^128 or more is infinity.                        */
+static uint16_t f64_to_bf16(double v) {
+    if (isnan(v)) return 0x7FC0u;
+    const uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    const double a = fabs(v);
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);                                   /* a = m 2^e, m in [0.5, 1) */
+    int unit = e - 8;
+    if (unit < -133) unit = -133;
+    const double r = ldexp(nearbyint(ldexp(a, -unit)), unit);   /* default mode: ties to even */
+    const float f = (float)r;                       /* exact, or infinity past FP32's range */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(sign | ((u >> 16) & 0x7FFFu));
+}
+
+int oracle_swiglu_bf16(const uint16_t* gu, int64_t M, int64_t F, uint16_t* h, int threads) {
+    if (M < 0 || F < 0) return ORACLE_ERR_SHAPE;
+    if ((M > 0 && F > 0) && (!gu || !h)) return ORACLE_ERR_ARG;
+    for (int64_t e = 0; e < M * 2 * F; ++e)
+        if (!isfinite(bf16_to_f32(gu[e]))) return ORACLE_ERR_NONFINITE;
+    set_threads(threads);
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t f = 0; f < F; ++f) {
+            const double g = (double)bf16_to_f32(gu[m * 2 * F + f]);
+            const double u = (double)bf16_to_f32(gu[m * 2 * F + F + f]);
+            const double silu = g / (1.0 + exp(-g));
+            h[m * F + f] = f64_to_bf16(silu * u);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------- */
 /* BF16 GEMM, the unquantized comparator of the FP8 path (the report weighs   */
 /* its FP8 training against BF16 training of the same model):                 */
 /*     out[i][j] = sum_k a(i,k) * b(j,k),  a = A [I,K], b = B [J,K] BF16 bits. */

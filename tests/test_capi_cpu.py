@@ -39,7 +39,7 @@ def L():
 
 def test_exports_every_header_symbol(L):
     names = header_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -86,6 +86,18 @@ def test_quantizer_argument_errors(L):
     assert L.fp8_quantize_dual(A16, 128, 128, A16, A16, None, A16, None) == NULL
     assert L.fp8_quantize_dual(A16, 128, 128, A16, A16, MIS, A16, None) == ALIGN
     assert L.fp8_quantize_dual(None, 0, 128, None, None, None, None, None) == OK
+
+    # gate/up [M, 2F] -> H's codes; h (BF16 H) is optional
+    assert L.fp8_swiglu_quantize_dual(A16, 100, 128, A16, A16, A16, A16, None, None) == SHAPE
+    assert L.fp8_swiglu_quantize_dual(A16, 128, 192, A16, A16, A16, A16, None, None) == SHAPE
+    assert L.fp8_swiglu_quantize_dual(None, 128, 128, A16, A16, A16, A16, None, None) == NULL
+    assert L.fp8_swiglu_quantize_dual(A16, 128, 128, A16, None, A16, A16, None, None) == NULL
+    assert L.fp8_swiglu_quantize_dual(A16, 128, 128, A16, A16, A16, None, None, None) == NULL
+    assert L.fp8_swiglu_quantize_dual(MIS, 128, 128, A16, A16, A16, A16, None, None) == ALIGN
+    assert L.fp8_swiglu_quantize_dual(A16, 128, 128, A16, A16, A16, A16, MIS, None) == ALIGN
+    assert L.fp8_swiglu_quantize_dual(A16, 128, 128, A16, A16 + 2, A16, A16, None, None) == ALIGN
+    assert L.fp8_swiglu_quantize_dual(None, 0, 128, None, None, None, None, None, None) == OK
+    assert L.fp8_swiglu_quantize_dual(None, 128, 0, None, None, None, None, None, None) == OK
 
     assert L.fp8_encode_e4m3(A16, -1, A16, None) == SHAPE
     assert L.fp8_encode_e4m3(None, 4, A16, None) == NULL
@@ -263,6 +275,11 @@ def test_binding_rejects_mismatched_inputs_before_any_call(monkeypatch):
         ("x", lambda: B.fp8_quantize_block(E((128, 256), f32))),
         ("x", lambda: B.fp8_quantize_transposed(E((128, 256, 1), bf))),
         ("x", lambda: B.fp8_quantize_dual(E((256, 128), bf)[:, ::2])),
+        ("gate_up", lambda: B.fp8_swiglu_quantize_dual(E((256, 256), f32))),
+        ("gate_up", lambda: B.fp8_swiglu_quantize_dual(E((256, 255), bf))),
+        ("gate_up", lambda: B.fp8_swiglu_quantize_dual(E((256, 512), bf)[:, ::2])),
+        ("h", lambda: B.fp8_swiglu_quantize_dual(E((256, 256), bf), h=E((256, 256), bf))),
+        ("qt", lambda: B.fp8_swiglu_quantize_dual(E((256, 256), bf), qt=E((256, 128), u8))),
         ("output", lambda: B.fp8_gemm_fprop(xq, xs, wq, ws, y=E((256, 64), bf))),
         ("workspace", lambda: B.fp8_gemm_wgrad(xq, xs, E((128, 256), u8), E((128, 2), f32),
                                                workspace=E((64,), f32))),

@@ -1,0 +1,97 @@
+"""fp8_swiglu_quantize_dual through the C ABI, against the oracle.
+
+The kernel forms H = silu(gate) * up in FP32 with the hardware exponential and
+reciprocal and rounds it to BF16; the oracle forms it in double and rounds
+once.  The gate on H: every element within one BF16 unit of the oracle's
+(nearly all equal).  The codes and scales are a decision taken from H, so they
+are compared bit for bit with the oracle's quantization of the H the kernel
+formed (returned through the optional h output): row tiles as
+oracle.quantize_rowtile(H), token-axis tiles as oracle.quantize_transposed(H).
+Without h the codes are the same bytes, and they equal fp8_quantize_dual of
+that H on the GPU."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp8_block_scaled_03_amd as fp8
+from fp8_block_scaled_03_amd import inputs
+from helpers import bf16_to_f64, bf16_ulp, to_dev_bf16, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _gate_up(M, F, key, gate_std=1.0):
+    g = inputs.normal((key, M, F), (M, F), gate_std)
+    u = inputs.normal((key + 1, M, F), (M, F), 1.0)
+    return np.ascontiguousarray(np.concatenate([g, u], axis=1))
+
+
+def _check(gu_bits, what, full_h_equal_frac=0.99):
+    M, F = gu_bits.shape[0], gu_bits.shape[1] // 2
+    gu = to_dev_bf16(gu_bits)
+    q, s, qt, st, h = fp8.fp8_swiglu_quantize_dual(gu, with_h=True)
+    q2, s2, qt2, st2, none = fp8.fp8_swiglu_quantize_dual(gu)
+    dq, ds, dqt, dst = fp8.fp8_quantize_dual(h)
+    torch.cuda.synchronize()
+    assert none is None
+    hk = to_np(h)
+    ho = oracle.swiglu(gu_bits)
+    diff = np.abs(bf16_to_f64(hk) - bf16_to_f64(ho))
+    ok = diff <= bf16_ulp(bf16_to_f64(ho))
+    eq = float((hk == ho).mean())
+    _say(f"{what} {M}x{F}: H equal {eq:.6f}, max diff/ulp "
+         f"{float((diff / bf16_ulp(bf16_to_f64(ho))).max()):.2f}")
+    assert ok.all(), f"{what}: {int((~ok).sum())} H elements more than one BF16 unit off"
+    assert eq >= full_h_equal_frac
+    oq, os_ = oracle.quantize_rowtile(hk)
+    oqt, ost = oracle.quantize_transposed(hk)
+    for name, got, want in (("q", q, oq), ("s", s, os_), ("qt", qt, oqt), ("st", st, ost)):
+        g = to_np(got)
+        if g.dtype == np.float32:
+            g, want = g.view(np.uint32), want.view(np.uint32)
+        assert np.array_equal(g, want), f"{what}: {name} differs from the oracle's quantization of H"
+    for a, b, name in ((q, q2, "q"), (s, s2, "s"), (qt, qt2, "qt"), (st, st2, "st"),
+                       (q, dq, "q vs dual"), (s, ds, "s vs dual"), (qt, dqt, "qt vs dual"),
+                       (st, dst, "st vs dual")):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"{what}: {name}"
+
+
+@pytest.mark.parametrize("M,F,std", [(256, 384, 1.0), (1024, 768, 3.0), (128, 128, 0.25)])
+def test_swiglu_dual_parity(M, F, std):
+    _check(_gate_up(M, F, 110, std), "swiglu")
+
+
+def test_swiglu_dual_special_values():
+    """Zero gates and ups (signed zeros), gates large enough that H is the
+    plain product, gates negative enough that H is a signed zero, and a
+    tile of all zeros (the amax floor)."""
+    M, F = 256, 256
+    gu = _gate_up(M, F, 112).copy()
+    gate, up = gu[:, :F], gu[:, F:]
+    bits = lambda v: inputs.bf16_bits(np.full(1, v, dtype=np.float32))[0]
+    gate[0, :64] = bits(0.0)
+    gate[0, 64:128] = bits(-0.0)
+    up[1, :128] = bits(0.0)
+    gate[2, :128] = bits(100.0)
+    gate[3, :128] = bits(-100.0)
+    gate[128:, 128:] = bits(0.0)                  # token-axis and row tiles that are all zero
+    _check(gu, "swiglu special", full_h_equal_frac=0.99)
+
+
+def test_swiglu_dual_empty():
+    for M, F in ((0, 256), (256, 0)):
+        gu = torch.empty((M, 2 * F), dtype=torch.bfloat16, device="cuda")
+        q, s, qt, st, h = fp8.fp8_swiglu_quantize_dual(gu, with_h=True)
+        torch.cuda.synchronize()
+        assert q.numel() == 0 and qt.numel() == 0 and h.numel() == 0
+
+
+def test_swiglu_dual_mlp_size():
+    """The down projection's input at the 8192-token MLP shape: gate/up
+    [8192, 12288] from N(0,1) activations, every element compared."""
+    _check(_gate_up(8192, inputs.FFN, 114), "swiglu mlp")
