@@ -128,8 +128,9 @@ fp8bs_status fp8_quantize_dual(const uint16_t* x, int64_t M, int64_t C, uint8_t*
 
 /*
  * SwiGLU with its output quantized on produce (Puro-2B report, section 2
- * "FP8": only the main linear matmuls run in FP8; elementwise work such as the
- * MLP's SwiGLU stays in BF16/FP32).  H = silu(G) * U is formed in FP32 and
+ * "FP8": only the main linear matmuls run in FP8 and the rest of the step
+ * keeps BF16/FP32 precision; in a Qwen3-style decoder, the shapes this
+ * library is sized for, the MLP's SwiGLU is such BF16 work).  H = silu(G) * U is formed in FP32 and
  * rounded to BF16, exactly where a separate SwiGLU kernel would round it, and
  * that BF16 H is quantized as fp8_quantize_dual(H) would quantize it: the
  * down projection's two operands (row tiles for its fprop, token-axis tiles
