@@ -1023,7 +1023,31 @@ def swiglu_quantization(torch, fp8, reps=5):
     # scale sets (2 x 4 B per 128 elements)
     algo = T * F * (4 + 2 + 8 / 128)
     rate = algo / (fused * 1e-3) / 1e9
-    del gu, q, s, qt, st, h
+    del q, s, qt, st, h
+    # backward: dH [T, F] and gate/up -> the gate/up gradient [T, 2F], both quantizations
+    dh = (torch.randn(T, F, device="cuda", generator=gen) * 1e-3).bfloat16()
+    q = torch.empty(T, 2 * F, device="cuda", dtype=torch.uint8)
+    s = torch.empty(T, 2 * F // 128, device="cuda", dtype=torch.float32)
+    qt = torch.empty(2 * F, T, device="cuda", dtype=torch.uint8)
+    st = torch.empty(2 * F, T // 128, device="cuda", dtype=torch.float32)
+    dgu = torch.empty(T, 2 * F, device="cuda", dtype=torch.bfloat16)
+
+    def separate_bwd():
+        g, u = gu[:, :F].float(), gu[:, F:].float()
+        sg = torch.sigmoid(g)
+        d = dh.float()
+        dgu[:, :F] = d * u * (sg * (1 + g * (1 - sg)))
+        dgu[:, F:] = d * (g * sg)
+        fp8.fp8_quantize_dual(dgu, q, s, qt, st)
+
+    sep_b = _time_events(torch, separate_bwd, reps)
+    fused_b = _time_events(torch, lambda: fp8.fp8_swiglu_backward_quantize_dual(
+        dh, gu, q, s, qt, st), reps)
+    # read dH, gate and up once (3 B per element of the gradient), write both code
+    # sets and scale sets (2 + 8/128 B)
+    algo_b = T * 2 * F * (3 + 2 + 8 / 128)
+    rate_b = algo_b / (fused_b * 1e-3) / 1e9
+    del gu, dh, q, s, qt, st, dgu
     torch.cuda.empty_cache()
     return {"f3_swiglu_quantize_on_produce": {
         "workload": "the MLP's SwiGLU at 16384 tokens (gate/up [16384, 12288] bf16 -> H "
@@ -1031,7 +1055,13 @@ def swiglu_quantization(torch, fp8, reps=5):
         "separate_ms": round(sep, 4), "fused_ms": round(fused, 4),
         "fused_with_bf16_h_ms": round(fused_h, 4), "fused_speedup": round(sep / fused, 3),
         "fused_algorithmic_bytes": int(algo), "fused_gbs": round(rate, 1),
-        "fused_frac_hbm": round(rate / PEAK_HBM_GBS, 4)}}
+        "fused_frac_hbm": round(rate / PEAK_HBM_GBS, 4),
+        "backward": {
+            "workload": "its backward: dH [16384, 6144] and gate/up -> the gate/up gradient "
+                        "[16384, 12288] with both of its quantizations",
+            "separate_ms": round(sep_b, 4), "fused_ms": round(fused_b, 4),
+            "fused_speedup": round(sep_b / fused_b, 3), "fused_algorithmic_bytes": int(algo_b),
+            "fused_gbs": round(rate_b, 1), "fused_frac_hbm": round(rate_b / PEAK_HBM_GBS, 4)}}}
 
 
 def fp8_linear_comparison(torch, fp8, reps=5):

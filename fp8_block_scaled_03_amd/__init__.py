@@ -15,6 +15,6 @@ from ._binding import (FP8BS_OUT_BF16, FP8BS_OUT_F32, Fp8bsError, bf16_gemm_tn, 
                        fp8_gemm_wgrad_accumulate_workspace_bytes, fp8_gemm_wgrad_noalloc,
                        fp8_gemm_wgrad_workspace_bytes, fp8_quantize_block,
                        fp8_quantize_dual, fp8_quantize_rowtile, fp8_quantize_transposed,
-                       fp8_swiglu_quantize_dual,
+                       fp8_swiglu_backward_quantize_dual, fp8_swiglu_quantize_dual,
                        fp8bs_hbm_rate, fp8bs_mfma_rate, fp8bs_status_string, fp8bs_version)
 from .linear import Fp8Linear, Fp8LinearFunction  # noqa: F401

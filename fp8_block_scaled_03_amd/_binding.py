@@ -34,6 +34,7 @@ SIGNATURES = {
     "fp8_quantize_transposed": (_INT, [_P, _I64, _I64, _P, _P, _P]),
     "fp8_quantize_dual": (_INT, [_P, _I64, _I64, _P, _P, _P, _P, _P]),
     "fp8_swiglu_quantize_dual": (_INT, [_P, _I64, _I64, _P, _P, _P, _P, _P, _P]),
+    "fp8_swiglu_backward_quantize_dual": (_INT, [_P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P]),
     "fp8_gemm_fprop": (_INT, [_P, _P, _P, _P, _P, _INT, _I64, _I64, _I64, _P]),
     "fp8_gemm_dgrad": (_INT, [_P, _P, _P, _P, _P, _INT, _I64, _I64, _I64, _P]),
     "fp8_gemm_fprop_mfma8": (_INT, [_P, _P, _P, _P, _P, _INT, _I64, _I64, _I64, _P]),
@@ -257,6 +258,38 @@ def fp8_swiglu_quantize_dual(gate_up: torch.Tensor, q=None, s=None, qt=None, st=
         _ptr(gate_up), M, F, _ptr(q), _ptr(s), _ptr(qt), _ptr(st), _ptr(h),
         _stream(gate_up, stream)))
     return q, s, qt, st, h
+
+
+def fp8_swiglu_backward_quantize_dual(dh: torch.Tensor, gate_up: torch.Tensor, q=None, s=None,
+                                      qt=None, st=None, dgate_up=None, with_bf16: bool = False,
+                                      stream=None):
+    """dh bf16 [M,F], gate_up bf16 [M,2F] -> the gate/up gradient dGU [M,2F]
+    quantized on produce: (q [M,2F], s [M,2F/128], qt [2F,M], st [2F,M/128],
+    dgate_up bf16 [M,2F] or None).  dGU in BF16 only with with_bf16=True or a
+    given dgate_up."""
+    M, F = _dims(dh, "dh")
+    _need(dh, torch.bfloat16, (M, F), "dh")
+    _dims(gate_up, "gate_up")
+    _need(gate_up, torch.bfloat16, (M, 2 * F), "gate_up")
+    dev = dh.device
+    with _alloc_on(stream, dev):
+        q = torch.empty((M, 2 * F), dtype=torch.uint8, device=dev) if q is None else q
+        s = torch.empty((M, 2 * F // 128), dtype=torch.float32, device=dev) if s is None else s
+        qt = torch.empty((2 * F, M), dtype=torch.uint8, device=dev) if qt is None else qt
+        st = torch.empty((2 * F, M // 128), dtype=torch.float32, device=dev) if st is None else st
+        if with_bf16 and dgate_up is None:
+            dgate_up = torch.empty((M, 2 * F), dtype=torch.bfloat16, device=dev)
+    _need(q, torch.uint8, (M, 2 * F), "q")
+    _need(s, torch.float32, (M, _blocks(2 * F)), "s")
+    _need(qt, torch.uint8, (2 * F, M), "qt")
+    _need(st, torch.float32, (2 * F, _blocks(M)), "st")
+    if dgate_up is not None:
+        _need(dgate_up, torch.bfloat16, (M, 2 * F), "dgate_up")
+    _on_device(dh=dh, gate_up=gate_up, q=q, s=s, qt=qt, st=st, dgate_up=dgate_up)
+    _check("fp8_swiglu_backward_quantize_dual", capi().fp8_swiglu_backward_quantize_dual(
+        _ptr(dh), _ptr(gate_up), M, F, _ptr(q), _ptr(s), _ptr(qt), _ptr(st), _ptr(dgate_up),
+        _stream(dh, stream)))
+    return q, s, qt, st, dgate_up
 
 
 # ----------------------------------------------------------------------- GEMMs

@@ -174,6 +174,25 @@ fp8bs_status fp8_swiglu_quantize_dual(const uint16_t* gate_up, int64_t M, int64_
     return launched(fp8bs::launch_swiglu_dual(gate_up, M, F, q, s, qt, st, h, stream));
 }
 
+fp8bs_status fp8_swiglu_backward_quantize_dual(const uint16_t* dh, const uint16_t* gate_up,
+                                               int64_t M, int64_t F, uint8_t* q, float* s,
+                                               uint8_t* qt, float* st, uint16_t* dgate_up,
+                                               fp8bs_stream_t stream) {
+    if (!mult128(M) || !mult128(F)) return FP8BS_ERR_SHAPE;
+    const bool empty = (M == 0 || F == 0);
+    FP8BS_TRY(check_ptr(dh, empty, 16));
+    FP8BS_TRY(check_ptr(gate_up, empty, 16));
+    FP8BS_TRY(check_ptr(q, empty, 16));
+    FP8BS_TRY(check_ptr(s, empty, 4));
+    FP8BS_TRY(check_ptr(qt, empty, 16));
+    FP8BS_TRY(check_ptr(st, empty, 4));
+    if (dgate_up && !aligned(dgate_up, 16)) return FP8BS_ERR_ALIGN;
+    if (empty) return FP8BS_OK;
+    int cus;
+    FP8BS_TRY(check_device(&cus));
+    return launched(fp8bs::launch_swiglu_bwd_dual(dh, gate_up, M, F, q, s, qt, st, dgate_up, stream));
+}
+
 static fp8bs_status gemm_common(fp8bs::ScaleMode mode, const uint8_t* A, const float* sA,
                                 const uint8_t* B, const float* sB, void* C, int yt, int64_t I,
                                 int64_t J, int64_t Kc, void* workspace, size_t workspace_bytes,

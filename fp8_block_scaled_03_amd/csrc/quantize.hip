@@ -204,11 +204,12 @@ constexpr int kDualStrideDw = 72;                    // dwords per LDS token row
 __device__ __forceinline__ int dual_row(int r) { return ((r & 15) << 3) + (r >> 4); }
 
 // Where a thread's BF16 values come from: 8 consecutive channels (col ..
-// col+7) of token row `row`.  DualPlain reads them from X [M, C].
+// col+7) of token row `row`, the thread's i-th row of the tile (i = 0..3).
+// DualPlain reads them from X [M, C].
 struct DualPlain {
     const uint16_t* __restrict__ x;
     int64_t C;
-    __device__ __forceinline__ uint4 operator()(int64_t row, int64_t col) const {
+    __device__ __forceinline__ uint4 operator()(int, int64_t row, int64_t col) const {
         return load_stream16(x + row * C + col);
     }
 };
@@ -227,7 +228,7 @@ struct DualSwiglu {
     const uint16_t* __restrict__ gu;
     int64_t F;
     uint16_t* __restrict__ h;
-    __device__ __forceinline__ uint4 operator()(int64_t row, int64_t col) const {
+    __device__ __forceinline__ uint4 operator()(int, int64_t row, int64_t col) const {
         const uint16_t* p = gu + row * 2 * F + col;
         const uint4 g = load_stream16(p), u = load_stream16(p + F);
         uint4 r;
@@ -240,16 +241,84 @@ struct DualSwiglu {
     }
 };
 
+// SwiGLU backward, formed on the way in: for column f of H, the gate half of
+// the gate/up gradient [M, 2F] is d_gate = dh * u * silu'(g), silu'(g) =
+// s (1 + g (1 - s)) with s = 1 / (1 + e^-g), and the up half (column F + f)
+// is d_up = dh * silu(g) = dh * g * s, each rounded to BF16.  1 - s is taken
+// as e^-g * s for g >= 0 (no cancellation as s nears 1) and as 1 - s below
+// (where s < 1/2).  One workgroup quantizes the gate tile and then the up
+// tile of the same tokens and columns f: the first pass keeps the thread's dh
+// and g in registers for the second, so each input is read once.  The BF16
+// gradient is stored only when dgu is given.
+__device__ __forceinline__ float swiglu_bwd_gate_f32(float d, float g, float u) {
+    const float e = __expf(-g);
+    const float sg = __builtin_amdgcn_rcpf(1.0f + e);
+    const float om = g >= 0.0f ? e * sg : 1.0f - sg;
+    return d * u * (sg * (1.0f + g * om));
+}
+__device__ __forceinline__ float swiglu_bwd_up_f32(float d, float g) {
+    return d * (g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)));
+}
+struct SwigluBwdRegs {
+    uint4 d[4], g[4];
+};
+struct DualSwigluBwdGate {
+    const uint16_t* __restrict__ dh;
+    const uint16_t* __restrict__ gu;
+    int64_t F;
+    uint16_t* __restrict__ dgu;
+    SwigluBwdRegs* keep;
+    __device__ __forceinline__ uint4 operator()(int i, int64_t row, int64_t f) const {
+        const uint4 d = load_stream16(dh + row * F + f);
+        const uint4 g = load_stream16(gu + row * 2 * F + f);
+        const uint4 u = load_stream16(gu + row * 2 * F + F + f);
+        keep->d[i] = d;
+        keep->g[i] = g;
+        uint4 r;
+        r.x = pack_bf16x2(swiglu_bwd_gate_f32(bf16_lo(d.x), bf16_lo(g.x), bf16_lo(u.x)),
+                          swiglu_bwd_gate_f32(bf16_hi(d.x), bf16_hi(g.x), bf16_hi(u.x)));
+        r.y = pack_bf16x2(swiglu_bwd_gate_f32(bf16_lo(d.y), bf16_lo(g.y), bf16_lo(u.y)),
+                          swiglu_bwd_gate_f32(bf16_hi(d.y), bf16_hi(g.y), bf16_hi(u.y)));
+        r.z = pack_bf16x2(swiglu_bwd_gate_f32(bf16_lo(d.z), bf16_lo(g.z), bf16_lo(u.z)),
+                          swiglu_bwd_gate_f32(bf16_hi(d.z), bf16_hi(g.z), bf16_hi(u.z)));
+        r.w = pack_bf16x2(swiglu_bwd_gate_f32(bf16_lo(d.w), bf16_lo(g.w), bf16_lo(u.w)),
+                          swiglu_bwd_gate_f32(bf16_hi(d.w), bf16_hi(g.w), bf16_hi(u.w)));
+        if (dgu) *reinterpret_cast<uint4*>(dgu + row * 2 * F + f) = r;
+        return r;
+    }
+};
+struct DualSwigluBwdUp {
+    int64_t F;
+    uint16_t* __restrict__ dgu;
+    const SwigluBwdRegs* keep;
+    __device__ __forceinline__ uint4 operator()(int i, int64_t row, int64_t col) const {
+        const uint4 d = keep->d[i], g = keep->g[i];
+        uint4 r;
+        r.x = pack_bf16x2(swiglu_bwd_up_f32(bf16_lo(d.x), bf16_lo(g.x)),
+                          swiglu_bwd_up_f32(bf16_hi(d.x), bf16_hi(g.x)));
+        r.y = pack_bf16x2(swiglu_bwd_up_f32(bf16_lo(d.y), bf16_lo(g.y)),
+                          swiglu_bwd_up_f32(bf16_hi(d.y), bf16_hi(g.y)));
+        r.z = pack_bf16x2(swiglu_bwd_up_f32(bf16_lo(d.z), bf16_lo(g.z)),
+                          swiglu_bwd_up_f32(bf16_hi(d.z), bf16_hi(g.z)));
+        r.w = pack_bf16x2(swiglu_bwd_up_f32(bf16_lo(d.w), bf16_lo(g.w)),
+                          swiglu_bwd_up_f32(bf16_hi(d.w), bf16_hi(g.w)));
+        if (dgu) *reinterpret_cast<uint4*>(dgu + row * 2 * F + col) = r;
+        return r;
+    }
+};
+
+// One 128 x 128 tile (token block mb, channel block cb of C channels): its
+// row tiles and token-axis tiles.  `tile` is the workgroup's LDS tile and
+// `tab` its scale tables (loaded by the caller; the first barrier below
+// publishes them).
 template <bool ROWS, class Src>
-__device__ __forceinline__ void dual_tile(const Src& src, int64_t M, int64_t C,
-                                          uint8_t* __restrict__ q, float* __restrict__ s,
-                                          uint8_t* __restrict__ qt, float* __restrict__ st) {
-    __shared__ __align__(16) uint32_t tile[kTile * kDualStrideDw];
-    __shared__ ScaleTables tab;
-    load_scale_tables(&tab);
+__device__ __forceinline__ void dual_tile(const Src& src, int64_t M, int64_t C, int64_t mb,
+                                          int64_t cb, uint32_t* __restrict__ tile,
+                                          const ScaleTables& tab, uint8_t* __restrict__ q,
+                                          float* __restrict__ s, uint8_t* __restrict__ qt,
+                                          float* __restrict__ st) {
     const int tid = threadIdx.x;
     const int64_t cblocks = C / kTile;
-    const int64_t mb = blockIdx.x / cblocks, cb = blockIdx.x % cblocks;
     const int64_t m0 = mb * kTile, c0 = cb * kTile;
     const int chunk = tid & 15;                         // 8 channels: 8*chunk .. +7
     const int rsub = tid >> 4;                          // rows rsub + 32q
@@ -257,7 +326,7 @@ __device__ __forceinline__ void dual_tile(const Src& src, int64_t M, int64_t C,
     uint4 v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        v[i] = src(m0 + 32 * i + rsub, c0 + chunk * 8);
+        v[i] = src(i, m0 + 32 * i + rsub, c0 + chunk * 8);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 32 * i + rsub;
@@ -326,14 +395,58 @@ template <bool ROWS>
 __global__ __launch_bounds__(kDualThreads) void quant_dual_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t C, uint8_t* __restrict__ q,
     float* __restrict__ s, uint8_t* __restrict__ qt, float* __restrict__ st) {
-    dual_tile<ROWS>(DualPlain{x, C}, M, C, q, s, qt, st);
+    __shared__ __align__(16) uint32_t tile[kTile * kDualStrideDw];
+    __shared__ ScaleTables tab;
+    load_scale_tables(&tab);
+    const int64_t cblocks = C / kTile;
+    dual_tile<ROWS>(DualPlain{x, C}, M, C, blockIdx.x / cblocks, blockIdx.x % cblocks, tile, tab,
+                    q, s, qt, st);
 }
 
 __global__ __launch_bounds__(kDualThreads) void swiglu_dual_kernel(
     const uint16_t* __restrict__ gu, int64_t M, int64_t F, uint8_t* __restrict__ q,
     float* __restrict__ s, uint8_t* __restrict__ qt, float* __restrict__ st,
     uint16_t* __restrict__ h) {
-    dual_tile<true>(DualSwiglu{gu, F, h}, M, F, q, s, qt, st);
+    __shared__ __align__(16) uint32_t tile[kTile * kDualStrideDw];
+    __shared__ ScaleTables tab;
+    load_scale_tables(&tab);
+    const int64_t fblocks = F / kTile;
+    dual_tile<true>(DualSwiglu{gu, F, h}, M, F, blockIdx.x / fblocks, blockIdx.x % fblocks, tile,
+                    tab, q, s, qt, st);
+}
+
+__global__ __launch_bounds__(kDualThreads) void swiglu_bwd_dual_kernel(
+    const uint16_t* __restrict__ dh, const uint16_t* __restrict__ gu, int64_t M, int64_t F,
+    uint8_t* __restrict__ q, float* __restrict__ s, uint8_t* __restrict__ qt,
+    float* __restrict__ st, uint16_t* __restrict__ dgu) {
+    __shared__ __align__(16) uint32_t tile[kTile * kDualStrideDw];
+    __shared__ ScaleTables tab;
+    load_scale_tables(&tab);
+    const int64_t fblocks = F / kTile;
+    const int64_t mb = blockIdx.x / fblocks, fb = blockIdx.x % fblocks;
+    SwigluBwdRegs keep;
+    dual_tile<true>(DualSwigluBwdGate{dh, gu, F, dgu, &keep}, M, 2 * F, mb, fb, tile, tab, q, s,
+                    qt, st);
+    __syncthreads();              // every thread is done with the LDS tile of the gate pass
+    // The kept values pass through an empty asm statement after the barrier,
+    // so the up pass's arithmetic is not hoisted into the gate pass (where
+    // its results would hold registers across the whole pass).
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        asm volatile("" : "+v"(keep.d[i].x), "+v"(keep.d[i].y), "+v"(keep.d[i].z), "+v"(keep.d[i].w));
+        asm volatile("" : "+v"(keep.g[i].x), "+v"(keep.g[i].y), "+v"(keep.g[i].z), "+v"(keep.g[i].w));
+    }
+    dual_tile<true>(DualSwigluBwdUp{F, dgu, &keep}, M, 2 * F, mb, fblocks + fb, tile, tab, q, s,
+                    qt, st);
+}
+
+hipError_t launch_swiglu_bwd_dual(const uint16_t* dh, const uint16_t* gu, int64_t M, int64_t F,
+                                  uint8_t* q, float* s, uint8_t* qt, float* st, uint16_t* dgu,
+                                  hipStream_t stream) {
+    int64_t blocks = (M / kTile) * (F / kTile);
+    if (blocks == 0) return hipSuccess;
+    return launch(swiglu_bwd_dual_kernel, dim3((unsigned)blocks), dim3(kDualThreads), stream, dh,
+                  gu, M, F, q, s, qt, st, dgu);
 }
 
 hipError_t launch_swiglu_dual(const uint16_t* gu, int64_t M, int64_t F, uint8_t* q, float* s,

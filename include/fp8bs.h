@@ -151,6 +151,27 @@ fp8bs_status fp8_swiglu_quantize_dual(const uint16_t* gate_up, int64_t M, int64_
                                       fp8bs_stream_t stream);
 
 /*
+ * The SwiGLU's backward with its output quantized on produce (same passage:
+ * the elementwise backward stays in BF16/FP32; its result, the gradient of
+ * the gate/up projection's output, is the dY of that projection's FP8 dgrad
+ * and wgrad, which need both of its quantizations).
+ *   dh      bf16 [M, F]   gradient of H = silu(G) * U
+ *   gate_up bf16 [M, 2F]  the forward's input (G | U)
+ *   q   u8   [M, 2F], s  f32 [M, 2F/128]     row tiles of dGU
+ *   qt  u8   [2F, M], st f32 [2F, M/128]     token-axis tiles of dGU
+ *   dgate_up bf16 [M, 2F] or NULL            dGU itself, when given
+ * dGU[:, f] = dh * u * silu'(g) (gate half), dGU[:, F + f] = dh * silu(g)
+ * (up half), silu'(g) = s (1 + g (1 - s)), s = 1 / (1 + e^-g), each formed in
+ * FP32 with the hardware exponential and reciprocal and rounded to BF16; the
+ * codes are those of fp8_quantize_dual applied to that BF16 dGU.
+ * M, F >= 0 and multiples of 128.  Inputs must be finite.
+ */
+fp8bs_status fp8_swiglu_backward_quantize_dual(const uint16_t* dh, const uint16_t* gate_up,
+                                               int64_t M, int64_t F, uint8_t* q, float* s,
+                                               uint8_t* qt, float* st, uint16_t* dgate_up,
+                                               fp8bs_stream_t stream);
+
+/*
  * fprop GEMM: Y = X W^T (Puro-2B report, section 2 "FP8": the forward matmul
  * of a main linear layer in FP8).
  *   xq  u8  [M, K],  xs f32 [M, K/128]          from fp8_quantize_rowtile(X)

@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_gemm.argtypes = [ctypes.c_int, P, P, P, P, i64, i64, i64, P, i64, P, ctypes.c_int]
         L.oracle_swiglu_bf16.restype = ctypes.c_int
         L.oracle_swiglu_bf16.argtypes = [P, i64, i64, P, ctypes.c_int]
+        L.oracle_swiglu_backward_bf16.restype = ctypes.c_int
+        L.oracle_swiglu_backward_bf16.argtypes = [P, P, i64, i64, P, ctypes.c_int]
         L.oracle_gemm_bf16.restype = ctypes.c_int
         L.oracle_gemm_bf16.argtypes = [P, P, i64, i64, i64, P, i64, P, ctypes.c_int]
         L.oracle_version.restype = ctypes.c_int
@@ -183,6 +185,20 @@ def swiglu(gu: np.ndarray, threads: int = 0) -> np.ndarray:
     h = np.empty((M, F2 // 2), dtype=np.uint16)
     _check(lib().oracle_swiglu_bf16(_ptr(gu), M, F2 // 2, _ptr(h), threads), "swiglu")
     return h
+
+
+def swiglu_backward(dh: np.ndarray, gu: np.ndarray, threads: int = 0) -> np.ndarray:
+    """dH bf16 bits [M, F] and gate/up bf16 bits [M, 2F] -> the gate/up
+    gradient [M, 2F] as bf16 bits: d_gate = dH * up * silu'(gate) in the first
+    F columns, d_up = dH * silu(gate) in the last F (double, one rounding)."""
+    dh, gu = _u16(dh), _u16(gu)
+    M, F = dh.shape
+    if gu.shape != (M, 2 * F):
+        raise ValueError("gate/up input must be [M, 2F] for dH [M, F]")
+    out = np.empty((M, 2 * F), dtype=np.uint16)
+    _check(lib().oracle_swiglu_backward_bf16(_ptr(dh), _ptr(gu), M, F, _ptr(out), threads),
+           "swiglu backward")
+    return out
 
 
 # ------------------------------------------------------------------------- GEMMs

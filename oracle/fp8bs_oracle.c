@@ -376,6 +376,34 @@ int oracle_swiglu_bf16(const uint16_t* gu, int64_t M, int64_t F, uint16_t* h, in
     return ORACLE_OK;
 }
 
+/* SwiGLU backward: from the gradient dh of H = silu(g) * u,                  */
+/*     d_gate = dh * u * silu'(g),  silu'(g) = s (1 + g (1 - s)),  s = 1/(1+e^-g) */
+/*     d_up   = dh * silu(g),                                                  */
+/* written as the gradient of the gate/up output [M, 2F] (d_gate in columns   */
+/* 0..F-1, d_up in F..2F-1).  Double, one rounding to BF16 per element.       */
+int oracle_swiglu_backward_bf16(const uint16_t* dh, const uint16_t* gu, int64_t M, int64_t F,
+                                uint16_t* dgu, int threads) {
+    if (M < 0 || F < 0) return ORACLE_ERR_SHAPE;
+    if ((M > 0 && F > 0) && (!dh || !gu || !dgu)) return ORACLE_ERR_ARG;
+    for (int64_t e = 0; e < M * F; ++e)
+        if (!isfinite(bf16_to_f32(dh[e]))) return ORACLE_ERR_NONFINITE;
+    for (int64_t e = 0; e < M * 2 * F; ++e)
+        if (!isfinite(bf16_to_f32(gu[e]))) return ORACLE_ERR_NONFINITE;
+    set_threads(threads);
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t f = 0; f < F; ++f) {
+            const double d = (double)bf16_to_f32(dh[m * F + f]);
+            const double g = (double)bf16_to_f32(gu[m * 2 * F + f]);
+            const double u = (double)bf16_to_f32(gu[m * 2 * F + F + f]);
+            const double sig = 1.0 / (1.0 + exp(-g));
+            dgu[m * 2 * F + f] = f64_to_bf16(d * u * (sig * (1.0 + g * (1.0 - sig))));
+            dgu[m * 2 * F + F + f] = f64_to_bf16(d * (g * sig));
+        }
+    }
+    return ORACLE_OK;
+}
+
 /* ------------------------------------------------------------------------- */
 /* BF16 GEMM, the unquantized comparator of the FP8 path (the report weighs   */
 /* its FP8 training against BF16 training of the same model):                 */

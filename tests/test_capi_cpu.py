@@ -39,7 +39,7 @@ def L():
 
 def test_exports_every_header_symbol(L):
     names = header_functions()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -98,6 +98,18 @@ def test_quantizer_argument_errors(L):
     assert L.fp8_swiglu_quantize_dual(A16, 128, 128, A16, A16 + 2, A16, A16, None, None) == ALIGN
     assert L.fp8_swiglu_quantize_dual(None, 0, 128, None, None, None, None, None, None) == OK
     assert L.fp8_swiglu_quantize_dual(None, 128, 0, None, None, None, None, None, None) == OK
+
+    # dH [M, F] and gate/up [M, 2F] -> the gate/up gradient's codes; its BF16 copy optional
+    bw = L.fp8_swiglu_backward_quantize_dual
+    assert bw(A16, A16, 100, 128, A16, A16, A16, A16, None, None) == SHAPE
+    assert bw(A16, A16, 128, 64, A16, A16, A16, A16, None, None) == SHAPE
+    assert bw(None, A16, 128, 128, A16, A16, A16, A16, None, None) == NULL
+    assert bw(A16, None, 128, 128, A16, A16, A16, A16, None, None) == NULL
+    assert bw(A16, A16, 128, 128, A16, A16, None, A16, None, None) == NULL
+    assert bw(A16, MIS, 128, 128, A16, A16, A16, A16, None, None) == ALIGN
+    assert bw(A16, A16, 128, 128, A16, A16, A16, A16, MIS, None) == ALIGN
+    assert bw(A16, A16, 128, 128, A16, A16, A16, A16 + 1, None, None) == ALIGN
+    assert bw(None, None, 0, 128, None, None, None, None, None, None) == OK
 
     assert L.fp8_encode_e4m3(A16, -1, A16, None) == SHAPE
     assert L.fp8_encode_e4m3(None, 4, A16, None) == NULL
@@ -280,6 +292,12 @@ def test_binding_rejects_mismatched_inputs_before_any_call(monkeypatch):
         ("gate_up", lambda: B.fp8_swiglu_quantize_dual(E((256, 512), bf)[:, ::2])),
         ("h", lambda: B.fp8_swiglu_quantize_dual(E((256, 256), bf), h=E((256, 256), bf))),
         ("qt", lambda: B.fp8_swiglu_quantize_dual(E((256, 256), bf), qt=E((256, 128), u8))),
+        ("gate_up", lambda: B.fp8_swiglu_backward_quantize_dual(E((256, 128), bf), E((256, 128), bf))),
+        ("dh", lambda: B.fp8_swiglu_backward_quantize_dual(E((256, 128), f32), E((256, 256), bf))),
+        ("dgate_up", lambda: B.fp8_swiglu_backward_quantize_dual(
+            E((256, 128), bf), E((256, 256), bf), dgate_up=E((256, 128), bf))),
+        ("s", lambda: B.fp8_swiglu_backward_quantize_dual(
+            E((256, 128), bf), E((256, 256), bf), s=E((256, 1), f32))),
         ("output", lambda: B.fp8_gemm_fprop(xq, xs, wq, ws, y=E((256, 64), bf))),
         ("workspace", lambda: B.fp8_gemm_wgrad(xq, xs, E((128, 256), u8), E((128, 2), f32),
                                                workspace=E((64,), f32))),

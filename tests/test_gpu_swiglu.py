@@ -1,4 +1,5 @@
-"""fp8_swiglu_quantize_dual through the C ABI, against the oracle.
+"""fp8_swiglu_quantize_dual and fp8_swiglu_backward_quantize_dual through the
+C ABI, against the oracle.
 
 The kernel forms H = silu(gate) * up in FP32 with the hardware exponential and
 reciprocal and rounds it to BF16; the oracle forms it in double and rounds
@@ -8,7 +9,8 @@ are compared bit for bit with the oracle's quantization of the H the kernel
 formed (returned through the optional h output): row tiles as
 oracle.quantize_rowtile(H), token-axis tiles as oracle.quantize_transposed(H).
 Without h the codes are the same bytes, and they equal fp8_quantize_dual of
-that H on the GPU."""
+that H on the GPU.  The backward (the gate/up gradient from dH) is checked the
+same way, against the oracle's double-precision backward."""
 import numpy as np
 import pytest
 import torch
@@ -95,3 +97,62 @@ def test_swiglu_dual_mlp_size():
     """The down projection's input at the 8192-token MLP shape: gate/up
     [8192, 12288] from N(0,1) activations, every element compared."""
     _check(_gate_up(8192, inputs.FFN, 114), "swiglu mlp")
+
+
+# ------------------------------------------------------------------ backward
+def _check_bwd(dh_bits, gu_bits, what):
+    M, F = dh_bits.shape
+    dh, gu = to_dev_bf16(dh_bits), to_dev_bf16(gu_bits)
+    q, s, qt, st, d = fp8.fp8_swiglu_backward_quantize_dual(dh, gu, with_bf16=True)
+    q2, s2, qt2, st2, none = fp8.fp8_swiglu_backward_quantize_dual(dh, gu)
+    dq, ds, dqt, dst = fp8.fp8_quantize_dual(d)
+    torch.cuda.synchronize()
+    assert none is None
+    dk = to_np(d)
+    do = oracle.swiglu_backward(dh_bits, gu_bits)
+    want = bf16_to_f64(do)
+    diff = np.abs(bf16_to_f64(dk) - want)
+    ok = diff <= bf16_ulp(want)
+    eq_gate, eq_up = float((dk[:, :F] == do[:, :F]).mean()), float((dk[:, F:] == do[:, F:]).mean())
+    _say(f"{what} {M}x{F}: dGU equal gate {eq_gate:.6f} up {eq_up:.6f}")
+    assert ok.all(), f"{what}: {int((~ok).sum())} gradient elements more than one BF16 unit off"
+    assert min(eq_gate, eq_up) >= 0.99
+    oq, os_ = oracle.quantize_rowtile(dk)
+    oqt, ost = oracle.quantize_transposed(dk)
+    for name, got, want_q in (("q", q, oq), ("s", s, os_), ("qt", qt, oqt), ("st", st, ost)):
+        g = to_np(got)
+        if g.dtype == np.float32:
+            g, want_q = g.view(np.uint32), want_q.view(np.uint32)
+        assert np.array_equal(g, want_q), f"{what}: {name} differs from the oracle's quantization"
+    for a, b, name in ((q, q2, "q"), (s, s2, "s"), (qt, qt2, "qt"), (st, st2, "st"),
+                       (q, dq, "q vs dual"), (s, ds, "s vs dual"), (qt, dqt, "qt vs dual"),
+                       (st, dst, "st vs dual")):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"{what}: {name}"
+
+
+@pytest.mark.parametrize("M,F,std", [(256, 384, 1.0), (512, 256, 4.0)])
+def test_swiglu_backward_dual_parity(M, F, std):
+    dh = inputs.student_t((120, M, F), (M, F), 3.0, 1e-3)
+    _check_bwd(dh, _gate_up(M, F, 121, std), "swiglu backward")
+
+
+def test_swiglu_backward_dual_special_values():
+    M, F = 256, 256
+    dh = inputs.normal((123, M, F), (M, F), 1.0).copy()
+    gu = _gate_up(M, F, 124).copy()
+    bits = lambda v: inputs.bf16_bits(np.full(1, v, dtype=np.float32))[0]
+    gu[0, :128] = bits(0.0)                  # silu'(0) = 1/2, silu(0) = 0
+    gu[1, :128] = bits(100.0)                # silu' = 1
+    gu[2, :128] = bits(-100.0)               # both zero
+    gu[3, :128] = bits(-1.28125)             # next to the root of silu'
+    dh[4, :] = bits(0.0)
+    dh[128:, 128:] = bits(0.0)               # an all-zero tile of both halves
+    _check_bwd(dh, gu, "swiglu backward special")
+
+
+def test_swiglu_backward_dual_mlp_size():
+    """The gate/up projection's output gradient at the 8192-token MLP shape:
+    dH [8192, 6144] (Student-t, nu = 3, x 1e-3) and gate/up [8192, 12288]."""
+    M, F = 8192, inputs.FFN
+    dh = inputs.student_t((126, M, F), (M, F), 3.0, 1e-3)
+    _check_bwd(dh, _gate_up(M, F, 127), "swiglu backward mlp")

@@ -130,3 +130,81 @@ def test_rejects_non_finite_and_odd_width():
         oracle.swiglu(bad)
     with pytest.raises(ValueError):
         oracle.swiglu(np.zeros((2, 3), dtype=np.uint16))
+
+
+# ------------------------------------------------------------------ backward
+def _bwd(dh_bits, g_bits, u_bits):
+    return oracle.swiglu_backward(np.asarray(dh_bits, dtype=np.uint16).reshape(1, -1),
+                                  _gu(g_bits, u_bits))[0]
+
+
+def _silu64(g):
+    return g * expit(g)
+
+
+def test_backward_at_zero_gate():
+    """silu'(0) = 1/2 and silu(0) = 0: d_gate = dh*u/2 (an exact product
+    halved, rounded by torch) and d_up is a signed zero."""
+    rng = np.random.default_rng(7)
+    n = 512
+    dh, u = _bits(rng.normal(0, 1, n)), _bits(rng.normal(0, 1, n))
+    g = _bits(np.zeros(n))
+    out = _bwd(dh, g, u)
+    half = torch.from_numpy((_val(dh) * _val(u) / 2).astype(np.float32)).to(torch.bfloat16)
+    assert np.array_equal(out[:n], half.view(torch.int16).numpy().view(np.uint16))
+    assert np.all(_val(out[n:]) == 0.0)
+
+
+def test_backward_large_and_very_negative_gates():
+    rng = np.random.default_rng(8)
+    n = 256
+    dh, u = _bits(rng.normal(0, 1, n)), _bits(rng.normal(0, 1, n))
+    big = _bits(rng.uniform(90, 3000, n))
+    out = _bwd(dh, big, u)
+    as_bf16 = lambda x: torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(out[:n], as_bf16(_val(dh) * _val(u)))      # silu' = 1
+    assert np.array_equal(out[n:], as_bf16(_val(dh) * _val(big)))    # silu = g
+    neg = _bits(rng.uniform(-3000, -150, n))
+    out = _bwd(dh, neg, u)
+    assert np.all(_val(out) == 0.0)
+
+
+def test_backward_up_gradient_is_forward_with_unit_up():
+    """d_up = dh * silu(g): with dh = 1 it is the forward H for u = 1."""
+    rng = np.random.default_rng(9)
+    n = 2048
+    g = _bits(rng.normal(0, 3, n))
+    one = _bits(np.ones(n))
+    out = _bwd(one, g, _bits(rng.normal(0, 1, n)))
+    fwd = oracle.swiglu(_gu(g, one))[0]
+    assert np.array_equal(out[n:], fwd)
+
+
+@pytest.mark.parametrize("sigma", [0.5, 2.0, 6.0])
+def test_backward_against_central_differences(sigma):
+    """d_gate against dh*u*(silu(g+e) - silu(g-e))/(2e) in float64 (scipy's
+    logistic, e = 2^-20: truncation error ~1e-13 relative), d_up against
+    dh*g*expit(g); both within one BF16 unit, equal away from near ties."""
+    rng = np.random.default_rng(10)
+    n = 8192
+    dh, g, u = (_bits(rng.normal(0, 1, n)), _bits(rng.normal(0, sigma, n)),
+                _bits(rng.normal(0, 1, n)))
+    out = _bwd(dh, g, u)
+    gv, eps = _val(g), 2.0 ** -20
+    d_gate = _val(dh) * _val(u) * (_silu64(gv + eps) - _silu64(gv - eps)) / (2 * eps)
+    d_up = _val(dh) * _silu64(gv)
+    for got, want in ((out[:n], d_gate), (out[n:], d_up)):
+        diff = np.abs(_val(got) - want)
+        assert np.all(diff <= _ulp(want))
+        assert np.mean(got != _bits(want)) < 1e-2
+
+
+def test_backward_is_linear_in_dh():
+    rng = np.random.default_rng(11)
+    n = 2048
+    dh, g, u = (_bits(rng.normal(0, 1, n)), _bits(rng.normal(0, 2, n)),
+                _bits(rng.normal(0, 1, n)))
+    a = _bwd(dh, g, u)
+    b = _bwd(_bits(-2.0 * _val(dh)), g, u)
+    assert np.array_equal(_val(b), -2.0 * _val(a))
