@@ -1064,6 +1064,41 @@ def swiglu_quantization(torch, fp8, reps=5):
             "fused_gbs": round(rate_b, 1), "fused_frac_hbm": round(rate_b / PEAK_HBM_GBS, 4)}}}
 
 
+def rmsnorm_quantization(torch, fp8, reps=5):
+    """The RMSNorm in front of the QKV and MLP input projections at 16,384
+    tokens (X [16384, 2048]) with both quantizations of its output: torch's
+    BF16 rms_norm then fp8_quantize_dual, against fp8_rmsnorm_quantize_dual."""
+    T, C, eps = 16384, 2048, 1e-6
+    gen = torch.Generator(device="cuda").manual_seed(4)
+    x = torch.randn(T, C, device="cuda", generator=gen).bfloat16()
+    gamma = (torch.rand(C, device="cuda", generator=gen) + 0.5).bfloat16()
+    q = torch.empty(T, C, device="cuda", dtype=torch.uint8)
+    s = torch.empty(T, C // 128, device="cuda", dtype=torch.float32)
+    qt = torch.empty(C, T, device="cuda", dtype=torch.uint8)
+    st = torch.empty(C, T // 128, device="cuda", dtype=torch.float32)
+    r = torch.empty(T, device="cuda", dtype=torch.float32)
+
+    def separate():
+        y = torch.nn.functional.rms_norm(x, (C,), weight=gamma, eps=eps)
+        fp8.fp8_quantize_dual(y, q, s, qt, st)
+
+    sep = _time_events(torch, separate, reps)
+    fused = _time_events(torch, lambda: fp8.fp8_rmsnorm_quantize_dual(
+        x, gamma, eps, q, s, qt, st, r), reps)
+    # read x once (2 B per element), write both code sets and scale sets (2 + 8/128 B)
+    # and r (4 B per row); the fused form reads x twice (r first, then the tiles)
+    algo = T * C * (2 + 2 + 8 / 128) + 4 * T
+    rate = algo / (fused * 1e-3) / 1e9
+    del x, gamma, q, s, qt, st, r
+    torch.cuda.empty_cache()
+    return {"f3_rmsnorm_quantize_on_produce": {
+        "workload": "the RMSNorm of the QKV / MLP input at 16384 tokens (X [16384, 2048] bf16) "
+                    "with its output's row-tile and token-axis quantization",
+        "separate_ms": round(sep, 4), "fused_ms": round(fused, 4),
+        "fused_speedup": round(sep / fused, 3), "fused_algorithmic_bytes": int(algo),
+        "fused_gbs": round(rate, 1), "fused_frac_hbm": round(rate / PEAK_HBM_GBS, 4)}}
+
+
 def fp8_linear_comparison(torch, fp8, reps=5):
     """One decoder layer's four linears at 16,384 tokens, forward + backward:
     through Fp8Linear (the FP8 block-scaled path) and through torch's BF16
@@ -1321,6 +1356,7 @@ def main():
         result["next_rows"] = {**bf16_comparison(torch, fp8, cfg_obj, fp8_gemm_ms, mfma8_gemm_ms),
                                **dgrad_epilogue_quantization(torch, fp8, cfg_obj),
                                **swiglu_quantization(torch, fp8),
+                               **rmsnorm_quantization(torch, fp8),
                                **fp8_linear_comparison(torch, fp8)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity_sample"], parity8 = cpu_baseline(

@@ -1,7 +1,7 @@
 """FP8 block-scaled linear-layer path for AMD Instinct MI355X (gfx950).
 
 Quantizers (BF16 -> E4M3 codes + FP32 scales: 1x128 row tiles, 128x128
-weight blocks, token-axis tiles; SwiGLU quantized on produce) and
+weight blocks, token-axis tiles; RMSNorm and SwiGLU quantized on produce) and
 block-scaled FP8 GEMMs (fprop, dgrad, wgrad) in hand-written HIP kernels
 behind the C ABI of include/fp8bs.h.  The Python functions here carry the C
 names and only marshal arguments;
@@ -15,6 +15,7 @@ from ._binding import (FP8BS_OUT_BF16, FP8BS_OUT_F32, Fp8bsError, bf16_gemm_tn, 
                        fp8_gemm_wgrad_accumulate_workspace_bytes, fp8_gemm_wgrad_noalloc,
                        fp8_gemm_wgrad_workspace_bytes, fp8_quantize_block,
                        fp8_quantize_dual, fp8_quantize_rowtile, fp8_quantize_transposed,
-                       fp8_swiglu_backward_quantize_dual, fp8_swiglu_quantize_dual,
+                       fp8_rmsnorm_quantize_dual, fp8_swiglu_backward_quantize_dual,
+                       fp8_swiglu_quantize_dual,
                        fp8bs_hbm_rate, fp8bs_mfma_rate, fp8bs_status_string, fp8bs_version)
 from .linear import Fp8Linear, Fp8LinearFunction  # noqa: F401

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(PKG, "libfp8bs.so")
 FP8BS_OK = 0
 STATUS_NAMES = {0: "FP8BS_OK", 1: "FP8BS_ERR_NULL", 2: "FP8BS_ERR_SHAPE", 3: "FP8BS_ERR_ALIGN",
                 4: "FP8BS_ERR_DTYPE", 5: "FP8BS_ERR_WORKSPACE", 6: "FP8BS_ERR_HIP",
-                7: "FP8BS_ERR_UNSUPPORTED"}
+                7: "FP8BS_ERR_UNSUPPORTED", 8: "FP8BS_ERR_VALUE"}
 FP8BS_OUT_F32 = 0
 FP8BS_OUT_BF16 = 1
 
@@ -34,6 +34,8 @@ SIGNATURES = {
     "fp8_quantize_transposed": (_INT, [_P, _I64, _I64, _P, _P, _P]),
     "fp8_quantize_dual": (_INT, [_P, _I64, _I64, _P, _P, _P, _P, _P]),
     "fp8_swiglu_quantize_dual": (_INT, [_P, _I64, _I64, _P, _P, _P, _P, _P, _P]),
+    "fp8_rmsnorm_quantize_dual": (_INT, [_P, _P, ctypes.c_float, _I64, _I64, _P, _P, _P, _P, _P,
+                                         _P, _P]),
     "fp8_swiglu_backward_quantize_dual": (_INT, [_P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P]),
     "fp8_gemm_fprop": (_INT, [_P, _P, _P, _P, _P, _INT, _I64, _I64, _I64, _P]),
     "fp8_gemm_dgrad": (_INT, [_P, _P, _P, _P, _P, _INT, _I64, _I64, _I64, _P]),
@@ -258,6 +260,38 @@ def fp8_swiglu_quantize_dual(gate_up: torch.Tensor, q=None, s=None, qt=None, st=
         _ptr(gate_up), M, F, _ptr(q), _ptr(s), _ptr(qt), _ptr(st), _ptr(h),
         _stream(gate_up, stream)))
     return q, s, qt, st, h
+
+
+def fp8_rmsnorm_quantize_dual(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6, q=None,
+                              s=None, qt=None, st=None, rstd=None, y=None, with_y: bool = False,
+                              stream=None):
+    """x bf16 [M,C], gamma bf16 [C] -> Y = RMSNorm(x) * gamma quantized on
+    produce: (q [M,C], s [M,C/128], qt [C,M], st [C,M/128], rstd f32 [M],
+    y bf16 [M,C] or None).  Y in BF16 only with with_y=True or a given y."""
+    M, C = _dims(x, "x")
+    _need(x, torch.bfloat16, (M, C), "x")
+    _need(gamma, torch.bfloat16, (C,), "gamma")
+    dev = x.device
+    with _alloc_on(stream, dev):
+        q = torch.empty((M, C), dtype=torch.uint8, device=dev) if q is None else q
+        s = torch.empty((M, C // 128), dtype=torch.float32, device=dev) if s is None else s
+        qt = torch.empty((C, M), dtype=torch.uint8, device=dev) if qt is None else qt
+        st = torch.empty((C, M // 128), dtype=torch.float32, device=dev) if st is None else st
+        rstd = torch.empty((M,), dtype=torch.float32, device=dev) if rstd is None else rstd
+        if with_y and y is None:
+            y = torch.empty((M, C), dtype=torch.bfloat16, device=dev)
+    _need(q, torch.uint8, (M, C), "q")
+    _need(s, torch.float32, (M, _blocks(C)), "s")
+    _need(qt, torch.uint8, (C, M), "qt")
+    _need(st, torch.float32, (C, _blocks(M)), "st")
+    _need(rstd, torch.float32, (M,), "rstd")
+    if y is not None:
+        _need(y, torch.bfloat16, (M, C), "y")
+    _on_device(x=x, gamma=gamma, q=q, s=s, qt=qt, st=st, rstd=rstd, y=y)
+    _check("fp8_rmsnorm_quantize_dual", capi().fp8_rmsnorm_quantize_dual(
+        _ptr(x), _ptr(gamma), float(eps), M, C, _ptr(q), _ptr(s), _ptr(qt), _ptr(st), _ptr(rstd),
+        _ptr(y), _stream(x, stream)))
+    return q, s, qt, st, rstd, y
 
 
 def fp8_swiglu_backward_quantize_dual(dh: torch.Tensor, gate_up: torch.Tensor, q=None, s=None,

@@ -98,6 +98,7 @@ const char* fp8bs_status_string(fp8bs_status status) {
         case FP8BS_ERR_WORKSPACE: return "workspace too small";
         case FP8BS_ERR_HIP: return "HIP runtime error";
         case FP8BS_ERR_UNSUPPORTED: return "unsupported device (gfx950 required)";
+        case FP8BS_ERR_VALUE: return "scalar argument out of range";
     }
     return "unknown status";
 }
@@ -172,6 +173,27 @@ fp8bs_status fp8_swiglu_quantize_dual(const uint16_t* gate_up, int64_t M, int64_
     int cus;
     FP8BS_TRY(check_device(&cus));
     return launched(fp8bs::launch_swiglu_dual(gate_up, M, F, q, s, qt, st, h, stream));
+}
+
+fp8bs_status fp8_rmsnorm_quantize_dual(const uint16_t* x, const uint16_t* gamma, float eps,
+                                       int64_t M, int64_t C, uint8_t* q, float* s, uint8_t* qt,
+                                       float* st, float* rstd, uint16_t* y,
+                                       fp8bs_stream_t stream) {
+    if (!mult128(M) || !mult128(C)) return FP8BS_ERR_SHAPE;
+    if (!(eps >= 0.0f) || !(eps <= 3.4e38f)) return FP8BS_ERR_VALUE;
+    const bool empty = (M == 0 || C == 0);
+    FP8BS_TRY(check_ptr(x, empty, 16));
+    FP8BS_TRY(check_ptr(gamma, empty, 16));
+    FP8BS_TRY(check_ptr(q, empty, 16));
+    FP8BS_TRY(check_ptr(s, empty, 4));
+    FP8BS_TRY(check_ptr(qt, empty, 16));
+    FP8BS_TRY(check_ptr(st, empty, 4));
+    FP8BS_TRY(check_ptr(rstd, empty, 4));
+    if (y && !aligned(y, 16)) return FP8BS_ERR_ALIGN;
+    if (empty) return FP8BS_OK;
+    int cus;
+    FP8BS_TRY(check_device(&cus));
+    return launched(fp8bs::launch_rmsnorm_dual(x, gamma, eps, M, C, q, s, qt, st, rstd, y, stream));
 }
 
 fp8bs_status fp8_swiglu_backward_quantize_dual(const uint16_t* dh, const uint16_t* gate_up,

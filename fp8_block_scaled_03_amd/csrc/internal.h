@@ -44,6 +44,9 @@ hipError_t launch_quant_dual(const uint16_t* x, int64_t M, int64_t C, uint8_t* q
                              uint8_t* qt, float* st, hipStream_t stream);
 hipError_t launch_swiglu_dual(const uint16_t* gu, int64_t M, int64_t F, uint8_t* q, float* s,
                               uint8_t* qt, float* st, uint16_t* h, hipStream_t stream);
+hipError_t launch_rmsnorm_dual(const uint16_t* x, const uint16_t* gamma, float eps, int64_t M,
+                               int64_t C, uint8_t* q, float* s, uint8_t* qt, float* st,
+                               float* rstd, uint16_t* y, hipStream_t stream);
 hipError_t launch_swiglu_bwd_dual(const uint16_t* dh, const uint16_t* gu, int64_t M, int64_t F,
                                   uint8_t* q, float* s, uint8_t* qt, float* st, uint16_t* dgu,
                                   hipStream_t stream);

@@ -311,6 +311,29 @@ struct DualSwigluBwdUp {
 // row tiles and token-axis tiles.  `tile` is the workgroup's LDS tile and
 // `tab` its scale tables (loaded by the caller; the first barrier below
 // publishes them).
+// RMSNorm, formed on the way in: y = x * r * gamma in FP32, rounded to
+// BF16, with r = 1/sqrt(mean(x^2) + eps) of the token row, computed for every
+// row beforehand (rmsnorm_rstd_kernel).  y itself is stored only when given.
+struct DualRmsNorm {
+    const uint16_t* __restrict__ x;
+    int64_t C;
+    const uint16_t* __restrict__ gamma;
+    const float* __restrict__ rstd;
+    uint16_t* __restrict__ y;
+    __device__ __forceinline__ uint4 operator()(int, int64_t row, int64_t col) const {
+        const uint4 v = load_stream16(x + row * C + col);
+        const uint4 w = *reinterpret_cast<const uint4*>(gamma + col);
+        const float r = rstd[row];
+        uint4 o;
+        o.x = pack_bf16x2(bf16_lo(v.x) * r * bf16_lo(w.x), bf16_hi(v.x) * r * bf16_hi(w.x));
+        o.y = pack_bf16x2(bf16_lo(v.y) * r * bf16_lo(w.y), bf16_hi(v.y) * r * bf16_hi(w.y));
+        o.z = pack_bf16x2(bf16_lo(v.z) * r * bf16_lo(w.z), bf16_hi(v.z) * r * bf16_hi(w.z));
+        o.w = pack_bf16x2(bf16_lo(v.w) * r * bf16_lo(w.w), bf16_hi(v.w) * r * bf16_hi(w.w));
+        if (y) *reinterpret_cast<uint4*>(y + row * C + col) = o;
+        return o;
+    }
+};
+
 template <bool ROWS, class Src>
 __device__ __forceinline__ void dual_tile(const Src& src, int64_t M, int64_t C, int64_t mb,
                                           int64_t cb, uint32_t* __restrict__ tile,
@@ -438,6 +461,57 @@ __global__ __launch_bounds__(kDualThreads) void swiglu_bwd_dual_kernel(
     }
     dual_tile<true>(DualSwigluBwdUp{F, dgu, &keep}, M, 2 * F, mb, fblocks + fb, tile, tab, q, s,
                     qt, st);
+}
+
+// r = 1/sqrt(mean(x^2) + eps) per token row: one wave per row, each lane
+// summing the squares of its 16-byte pieces (columns 8l, 8l + 512, ...) in
+// FP32, then a butterfly over the wave; correctly rounded square root and
+// division.  Four rows per 256-thread workgroup.
+__global__ __launch_bounds__(256) void rmsnorm_rstd_kernel(const uint16_t* __restrict__ x,
+                                                           int64_t M, int64_t C, float eps,
+                                                           float* __restrict__ rstd) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;
+    const uint16_t* xr = x + row * C;
+    float ss = 0.f;
+    for (int64_t c = 8 * lane; c < C; c += 512) {
+        const uint4 v = load_stream16(xr + c);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float a = bf16_lo(w[j]), b = bf16_hi(w[j]);
+            ss = __builtin_fmaf(a, a, ss);
+            ss = __builtin_fmaf(b, b, ss);
+        }
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) ss += __shfl_xor(ss, o);
+    if (lane == 0) rstd[row] = 1.0f / sqrtf(ss / (float)C + eps);
+}
+
+__global__ __launch_bounds__(kDualThreads) void rmsnorm_dual_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
+    const float* __restrict__ rstd, int64_t M, int64_t C, uint8_t* __restrict__ q,
+    float* __restrict__ s, uint8_t* __restrict__ qt, float* __restrict__ st,
+    uint16_t* __restrict__ y) {
+    __shared__ __align__(16) uint32_t tile[kTile * kDualStrideDw];
+    __shared__ ScaleTables tab;
+    load_scale_tables(&tab);
+    const int64_t cblocks = C / kTile;
+    dual_tile<true>(DualRmsNorm{x, C, gamma, rstd, y}, M, C, blockIdx.x / cblocks,
+                    blockIdx.x % cblocks, tile, tab, q, s, qt, st);
+}
+
+hipError_t launch_rmsnorm_dual(const uint16_t* x, const uint16_t* gamma, float eps, int64_t M,
+                               int64_t C, uint8_t* q, float* s, uint8_t* qt, float* st,
+                               float* rstd, uint16_t* y, hipStream_t stream) {
+    if (M == 0 || C == 0) return hipSuccess;
+    hipError_t e = launch(rmsnorm_rstd_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), stream, x,
+                          M, C, eps, rstd);
+    if (e != hipSuccess) return e;
+    return launch(rmsnorm_dual_kernel, dim3((unsigned)((M / kTile) * (C / kTile))),
+                  dim3(kDualThreads), stream, x, gamma, (const float*)rstd, M, C, q, s, qt, st, y);
 }
 
 hipError_t launch_swiglu_bwd_dual(const uint16_t* dh, const uint16_t* gu, int64_t M, int64_t F,

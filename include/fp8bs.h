@@ -64,7 +64,8 @@ typedef enum {
     FP8BS_ERR_DTYPE = 4,       /* unknown output dtype */
     FP8BS_ERR_WORKSPACE = 5,   /* workspace given but too small */
     FP8BS_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed */
-    FP8BS_ERR_UNSUPPORTED = 7  /* the device is not gfx950 */
+    FP8BS_ERR_UNSUPPORTED = 7, /* the device is not gfx950 */
+    FP8BS_ERR_VALUE = 8        /* a scalar argument is out of its range */
 } fp8bs_status;
 
 typedef enum {
@@ -149,6 +150,29 @@ fp8bs_status fp8_quantize_dual(const uint16_t* x, int64_t M, int64_t C, uint8_t*
 fp8bs_status fp8_swiglu_quantize_dual(const uint16_t* gate_up, int64_t M, int64_t F, uint8_t* q,
                                       float* s, uint8_t* qt, float* st, uint16_t* h,
                                       fp8bs_stream_t stream);
+
+/*
+ * RMSNorm with its output quantized on produce (Puro-2B report, section 2
+ * "FP8": the FP8 path covers the main linear matmuls and the normalizations
+ * stay in BF16/FP32; in a Qwen3-style decoder an RMSNorm produces the input of
+ * the attention and MLP input projections, whose fprop and wgrad need its
+ * row tiles and token-axis tiles).
+ *   x     bf16 [M, C],  gamma bf16 [C],  eps >= 0 and finite
+ *   q   u8   [M, C],  s  f32 [M, C/128]      row tiles of Y
+ *   qt  u8   [C, M],  st f32 [C, M/128]      token-axis tiles of Y
+ *   rstd f32 [M]                             r of every row (the backward needs it)
+ *   y   bf16 [M, C] or NULL                  Y itself, when given
+ * r[m] = 1 / sqrt(mean_c x[m][c]^2 + eps) (squares summed in FP32, correctly
+ * rounded square root and division); Y = x * r * gamma in FP32, rounded to
+ * BF16; the codes are those of fp8_quantize_dual applied to that BF16 Y.
+ * Two launches on stream (r, then the quantized tiles).  M, C >= 0 and
+ * multiples of 128 (nothing is written when either is 0); FP8BS_ERR_VALUE
+ * for a negative or non-finite eps.
+ */
+fp8bs_status fp8_rmsnorm_quantize_dual(const uint16_t* x, const uint16_t* gamma, float eps,
+                                       int64_t M, int64_t C, uint8_t* q, float* s, uint8_t* qt,
+                                       float* st, float* rstd, uint16_t* y,
+                                       fp8bs_stream_t stream);
 
 /*
  * The SwiGLU's backward with its output quantized on produce (same passage:

@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_swiglu_bf16.argtypes = [P, i64, i64, P, ctypes.c_int]
         L.oracle_swiglu_backward_bf16.restype = ctypes.c_int
         L.oracle_swiglu_backward_bf16.argtypes = [P, P, i64, i64, P, ctypes.c_int]
+        L.oracle_rmsnorm_bf16.restype = ctypes.c_int
+        L.oracle_rmsnorm_bf16.argtypes = [P, P, ctypes.c_double, i64, i64, P, P, ctypes.c_int]
         L.oracle_gemm_bf16.restype = ctypes.c_int
         L.oracle_gemm_bf16.argtypes = [P, P, i64, i64, i64, P, i64, P, ctypes.c_int]
         L.oracle_version.restype = ctypes.c_int
@@ -199,6 +201,22 @@ def swiglu_backward(dh: np.ndarray, gu: np.ndarray, threads: int = 0) -> np.ndar
     _check(lib().oracle_swiglu_backward_bf16(_ptr(dh), _ptr(gu), M, F, _ptr(out), threads),
            "swiglu backward")
     return out
+
+
+# ------------------------------------------------------------------ RMSNorm
+def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float, threads: int = 0):
+    """x bf16 bits [M, C], gamma bf16 bits [C] -> (y bf16 bits [M, C],
+    r float32 [M]) with y = x * r * gamma, r = 1/sqrt(mean(x^2) + eps)
+    (double, one rounding of each output)."""
+    x, gamma = _u16(x), _u16(gamma)
+    M, C = x.shape
+    if gamma.shape != (C,):
+        raise ValueError("gamma must have one entry per channel")
+    y = np.empty((M, C), dtype=np.uint16)
+    r = np.empty(M, dtype=np.float32)
+    _check(lib().oracle_rmsnorm_bf16(_ptr(x), _ptr(gamma), float(eps), M, C, _ptr(y), _ptr(r),
+                                     threads), "rmsnorm")
+    return y, r
 
 
 # ------------------------------------------------------------------------- GEMMs

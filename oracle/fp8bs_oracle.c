@@ -405,6 +405,36 @@ int oracle_swiglu_backward_bf16(const uint16_t* dh, const uint16_t* gu, int64_t 
 }
 
 /* ------------------------------------------------------------------------- */
+/* RMSNorm, the BF16 op in front of the attention and MLP input projections:  */
+/*     y[m][c] = x[m][c] * r[m] * gamma[c],  r[m] = 1 / sqrt(mean_c x^2 + eps). */
+/* Double, one rounding of y to BF16; r is returned rounded to FP32.          */
+/* ------------------------------------------------------------------------- */
+int oracle_rmsnorm_bf16(const uint16_t* x, const uint16_t* gamma, double eps, int64_t M,
+                        int64_t C, uint16_t* y, float* rstd, int threads) {
+    if (M < 0 || C <= 0 || !(eps >= 0.0)) return ORACLE_ERR_SHAPE;
+    if (M > 0 && (!x || !gamma || !y || !rstd)) return ORACLE_ERR_ARG;
+    for (int64_t e = 0; e < M * C; ++e)
+        if (!isfinite(bf16_to_f32(x[e]))) return ORACLE_ERR_NONFINITE;
+    for (int64_t c = 0; c < C; ++c)
+        if (!isfinite(bf16_to_f32(gamma[c]))) return ORACLE_ERR_NONFINITE;
+    set_threads(threads);
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        double ss = 0.0;
+        for (int64_t c = 0; c < C; ++c) {
+            const double v = (double)bf16_to_f32(x[m * C + c]);
+            ss += v * v;
+        }
+        const double r = 1.0 / sqrt(ss / (double)C + eps);
+        rstd[m] = (float)r;
+        for (int64_t c = 0; c < C; ++c)
+            y[m * C + c] = f64_to_bf16((double)bf16_to_f32(x[m * C + c]) * r *
+                                       (double)bf16_to_f32(gamma[c]));
+    }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------- */
 /* BF16 GEMM, the unquantized comparator of the FP8 path (the report weighs   */
 /* its FP8 training against BF16 training of the same model):                 */
 /*     out[i][j] = sum_k a(i,k) * b(j,k),  a = A [I,K], b = B [J,K] BF16 bits. */

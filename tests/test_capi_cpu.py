@@ -39,7 +39,7 @@ def L():
 
 def test_exports_every_header_symbol(L):
     names = header_functions()
-    assert len(names) == 24, names
+    assert len(names) == 25, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -47,7 +47,7 @@ def test_exports_every_header_symbol(L):
 
 def test_version_and_status_strings(L):
     assert L.fp8bs_version() == 200
-    for st in range(8):
+    for st in range(9):
         s = L.fp8bs_status_string(st)
         assert s and isinstance(s, bytes)
     assert L.fp8bs_status_string(99) == b"unknown status"
@@ -98,6 +98,22 @@ def test_quantizer_argument_errors(L):
     assert L.fp8_swiglu_quantize_dual(A16, 128, 128, A16, A16 + 2, A16, A16, None, None) == ALIGN
     assert L.fp8_swiglu_quantize_dual(None, 0, 128, None, None, None, None, None, None) == OK
     assert L.fp8_swiglu_quantize_dual(None, 128, 0, None, None, None, None, None, None) == OK
+
+    # x [M, C], gamma [C] -> Y's codes and r; Y in BF16 optional; eps a finite value >= 0
+    rn = L.fp8_rmsnorm_quantize_dual
+    VALUE = 8
+    assert rn(A16, A16, 1e-6, 100, 128, A16, A16, A16, A16, A16, None, None) == SHAPE
+    assert rn(A16, A16, 1e-6, 128, 64, A16, A16, A16, A16, A16, None, None) == SHAPE
+    assert rn(A16, A16, -1.0, 128, 128, A16, A16, A16, A16, A16, None, None) == VALUE
+    assert rn(A16, A16, float("nan"), 128, 128, A16, A16, A16, A16, A16, None, None) == VALUE
+    assert rn(A16, A16, float("inf"), 128, 128, A16, A16, A16, A16, A16, None, None) == VALUE
+    assert rn(A16, None, 1e-6, 128, 128, A16, A16, A16, A16, A16, None, None) == NULL
+    assert rn(A16, A16, 1e-6, 128, 128, A16, A16, A16, A16, None, None, None) == NULL
+    assert rn(A16, MIS, 1e-6, 128, 128, A16, A16, A16, A16, A16, None, None) == ALIGN
+    assert rn(A16, A16, 1e-6, 128, 128, A16, A16, A16, A16, A16 + 2, None, None) == ALIGN
+    assert rn(A16, A16, 1e-6, 128, 128, A16, A16, A16, A16, A16, MIS, None) == ALIGN
+    assert rn(None, None, 1e-6, 0, 128, None, None, None, None, None, None, None) == OK
+    assert L.fp8bs_status_string(VALUE) == b"scalar argument out of range"
 
     # dH [M, F] and gate/up [M, 2F] -> the gate/up gradient's codes; its BF16 copy optional
     bw = L.fp8_swiglu_backward_quantize_dual
@@ -293,6 +309,11 @@ def test_binding_rejects_mismatched_inputs_before_any_call(monkeypatch):
         ("h", lambda: B.fp8_swiglu_quantize_dual(E((256, 256), bf), h=E((256, 256), bf))),
         ("qt", lambda: B.fp8_swiglu_quantize_dual(E((256, 256), bf), qt=E((256, 128), u8))),
         ("gate_up", lambda: B.fp8_swiglu_backward_quantize_dual(E((256, 128), bf), E((256, 128), bf))),
+        ("gamma", lambda: B.fp8_rmsnorm_quantize_dual(E((256, 128), bf), E((256,), bf))),
+        ("gamma", lambda: B.fp8_rmsnorm_quantize_dual(E((256, 128), bf), E((128,), f32))),
+        ("rstd", lambda: B.fp8_rmsnorm_quantize_dual(E((256, 128), bf), E((128,), bf),
+                                                      rstd=E((128,), f32))),
+        ("x", lambda: B.fp8_rmsnorm_quantize_dual(E((256, 256), bf)[:, :128], E((128,), bf))),
         ("dh", lambda: B.fp8_swiglu_backward_quantize_dual(E((256, 128), f32), E((256, 256), bf))),
         ("dgate_up", lambda: B.fp8_swiglu_backward_quantize_dual(
             E((256, 128), bf), E((256, 256), bf), dgate_up=E((256, 128), bf))),
