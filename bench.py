@@ -1148,6 +1148,50 @@ def fp8_linear_comparison(torch, fp8, reps=5):
         "fp8_mfma8_speedup_vs_torch_bf16": round(ms16 / ms8m, 3)}}
 
 
+def fp8_mlp_comparison(torch, fp8, reps=5):
+    """The decoder's MLP at 16,384 tokens (hidden 2048, FFN 6144), forward +
+    backward: Fp8SwiGLUMLP (both projections on the FP8 path, the SwiGLU and
+    its backward quantizing on produce) against torch's BF16 linear layers and
+    SwiGLU under autograd."""
+    T, d, F = 16384, 2048, 6144
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    mlp = fp8.Fp8SwiGLUMLP(d, F, device="cuda")
+    wgu = mlp.weight_gate_up.detach().clone().requires_grad_(True)
+    wd = mlp.weight_down.detach().clone().requires_grad_(True)
+    x = torch.randn(T, d, device="cuda", generator=gen).bfloat16().requires_grad_(True)
+    dy = (torch.randn(T, d, device="cuda", generator=gen) * 1e-3).bfloat16()
+
+    def fp8_mlp(mfma8):
+        def run():
+            x.grad = None
+            mlp.weight_gate_up.grad = mlp.weight_down.grad = None
+            mlp.mfma8 = mfma8
+            mlp(x).backward(dy)
+            mlp.mfma8 = False
+        return run
+
+    def bf16_mlp():
+        x.grad = wgu.grad = wd.grad = None
+        gu = torch.nn.functional.linear(x, wgu)
+        h = torch.nn.functional.silu(gu[:, :F]) * gu[:, F:]
+        torch.nn.functional.linear(h, wd).backward(dy)
+
+    flops = 3 * 2 * T * d * (3 * F)
+    ms8 = _time_events(torch, fp8_mlp(False), reps)
+    ms8m = _time_events(torch, fp8_mlp(True), reps)
+    ms16 = _time_events(torch, bf16_mlp, reps)
+    del mlp, wgu, wd, x, dy
+    torch.cuda.empty_cache()
+    return {"f4_fp8_swiglu_mlp": {
+        "workload": "the decoder's MLP at 16384 tokens (hidden 2048, FFN 6144: gate/up "
+                    "projection, SwiGLU, down projection), forward + backward",
+        "fp8_ms": round(ms8, 3), "fp8_tflops": round(flops / ms8 / 1e9, 1),
+        "torch_bf16_ms": round(ms16, 3), "torch_bf16_tflops": round(flops / ms16 / 1e9, 1),
+        "fp8_speedup_vs_torch_bf16": round(ms16 / ms8, 3),
+        "fp8_mfma8_ms": round(ms8m, 3), "fp8_mfma8_tflops": round(flops / ms8m / 1e9, 1),
+        "fp8_mfma8_speedup_vs_torch_bf16": round(ms16 / ms8m, 3)}}
+
+
 def mfma8_step(torch, plan, stream, fused, args, exact_value, layer0_fn):
     """The same step with the GEMMs whose block sums come from the FP8 matrix
     core (fp8_gemm_*_mfma8): their limited accumulation precision inside each
@@ -1357,7 +1401,8 @@ def main():
                                **dgrad_epilogue_quantization(torch, fp8, cfg_obj),
                                **swiglu_quantization(torch, fp8),
                                **rmsnorm_quantization(torch, fp8),
-                               **fp8_linear_comparison(torch, fp8)}
+                               **fp8_linear_comparison(torch, fp8),
+                               **fp8_mlp_comparison(torch, fp8)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity_sample"], parity8 = cpu_baseline(
             args.cpu_fraction, layer0, layer0_8)

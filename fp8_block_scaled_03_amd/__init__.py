@@ -5,7 +5,8 @@ weight blocks, token-axis tiles; RMSNorm and SwiGLU quantized on produce) and
 block-scaled FP8 GEMMs (fprop, dgrad, wgrad) in hand-written HIP kernels
 behind the C ABI of include/fp8bs.h.  The Python functions here carry the C
 names and only marshal arguments;
-``Fp8Linear`` is a bias-free linear layer built on them.
+``Fp8Linear`` is a bias-free linear layer built on them and ``Fp8SwiGLUMLP``
+the decoder's MLP.
 """
 from ._binding import (FP8BS_OUT_BF16, FP8BS_OUT_F32, Fp8bsError, bf16_gemm_tn, capi,  # noqa: F401
                        fp8_encode_e4m3, fp8_gemm_dgrad, fp8_gemm_dgrad_mfma8,
@@ -18,4 +19,5 @@ from ._binding import (FP8BS_OUT_BF16, FP8BS_OUT_F32, Fp8bsError, bf16_gemm_tn, 
                        fp8_rmsnorm_quantize_dual, fp8_swiglu_backward_quantize_dual,
                        fp8_swiglu_quantize_dual,
                        fp8bs_hbm_rate, fp8bs_mfma_rate, fp8bs_status_string, fp8bs_version)
-from .linear import Fp8Linear, Fp8LinearFunction  # noqa: F401
+from .linear import (Fp8Linear, Fp8LinearFunction, Fp8SwiGLUMLP,  # noqa: F401
+                     Fp8SwiGLUMLPFunction)
