@@ -64,6 +64,11 @@ def kernel_kind(name: str):
     import re
     if "splitk_reduce_kernel" in name:
         return "gemm_wgrad", False
+    if "rmsnorm_rstd_kernel" in name:               # the first launch of an RMSNorm call
+        return "rmsnorm_dual", False
+    for k in ("rmsnorm_dual", "swiglu_bwd_dual", "swiglu_dual"):
+        if k + "_kernel" in name:
+            return k, True
     m = re.search(r"gemm_bs_fp8(?:_big)?_kernel<(\d)", name)
     if m:
         return ("gemm_fprop", "gemm_dgrad", "gemm_wgrad")[int(m.group(1))], True
@@ -115,7 +120,7 @@ def summarize_rocprof(d: str) -> None:
                 kind, is_call = kernel_kind(r["Kernel_Name"])
                 if kind and kind.startswith("gemm_wgrad") and is_call:
                     last_wgrad = kind
-                elif kind and not is_call:
+                elif kind and not is_call and kind.startswith("gemm_wgrad"):
                     kind = last_wgrad
                 if kind:
                     k = per_kind.setdefault(kind, [0.0, 0])
@@ -180,13 +185,13 @@ def _pmc_dispatches(d: str, counter: str):
     return list(out.values())
 
 
-def record_traffic(fetch_dir: str, write_dir: str, out_path: str = TRAFFIC_FILE) -> None:
+def record_traffic(fetch_dir: str, write_dir: str, out_path: str | None = TRAFFIC_FILE) -> None:
     """HBM bytes per library call from two counter runs of the step (FETCH_SIZE
     and WRITE_SIZE, KiB per dispatch, each run made with --copy-calibration-mib
     1024).  Each counter is scaled by what it reads for that plain 1 GiB
     device copy; a wgrad call's bytes include its split-K reduction.  Writes
-    the per-kind records (keyed to the kernel sources' digest) and prints the
-    per-kernel lines."""
+    the per-kind records (keyed to the kernel sources' digest; not with out_path
+    None) and prints the per-kernel lines."""
     fetch = _pmc_dispatches(fetch_dir, "FETCH_SIZE")
     write = _pmc_dispatches(write_dir, "WRITE_SIZE")
     gib_kib = float(1 << 20)
@@ -221,8 +226,9 @@ def record_traffic(fetch_dir: str, write_dir: str, out_path: str = TRAFFIC_FILE)
             rec[kind] = {"bytes_per_launch": int(b / calls), "launches": calls,
                          "profile": "profiles/linear_set_hbm_bytes.txt",
                          "source_sha256_16": source_digest(kind)}
-    with open(out_path, "w") as f:
-        json.dump(rec, f, indent=1)
+    if out_path:
+        with open(out_path, "w") as f:
+            json.dump(rec, f, indent=1)
     print("# per library call (a wgrad call includes its split-K reduction)")
     for kind, r in sorted(rec.items()):
         print(f"{kind:20s} calls={r['launches']:5d} bytes_per_call={r['bytes_per_launch'] / 1e6:10.2f} MB")
@@ -254,6 +260,13 @@ def parse():
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from a FETCH_SIZE and a WRITE_SIZE "
                          "rocprofv3 run of the step and print the per-kernel bytes, then exit")
+    ap.add_argument("--producers", action="store_true",
+                    help="measure only the quantize-on-produce calls (RMSNorm, SwiGLU and its "
+                         "backward at 16384 tokens), print them as one JSON line and exit (for "
+                         "profiler runs of those kernels)")
+    ap.add_argument("--traffic-print-only", action="store_true",
+                    help="with --record-traffic: print the per-kernel bytes but leave "
+                         "profiles/traffic.json (which holds the step's records) as it is")
     ap.add_argument("--summarize-rocprof", metavar="DIR",
                     help="print a text summary of rocprofv3 CSV output in DIR and exit")
     return ap.parse_args()
@@ -1239,7 +1252,8 @@ def main():
         summarize_rocprof(args.summarize_rocprof)
         return
     if args.record_traffic:
-        record_traffic(*args.record_traffic)
+        record_traffic(*args.record_traffic,
+                       out_path=None if args.traffic_print_only else TRAFFIC_FILE)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the path is "
@@ -1256,6 +1270,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     fp8.capi()                                   # fails loudly if the library is missing
+    if args.producers:
+        if args.copy_calibration_mib:
+            n = args.copy_calibration_mib << 20
+            src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+            torch.empty_like(src).copy_(src)
+            torch.cuda.synchronize()
+            del src
+        print(json.dumps({**rmsnorm_quantization(torch, fp8), **swiglu_quantization(torch, fp8)}),
+              flush=True)
+        return
     plan = Plan(torch, fp8, inputs)
     stream = torch.cuda.current_stream()
     fused = args.quantizer == "fused"
