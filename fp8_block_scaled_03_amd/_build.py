@@ -23,6 +23,9 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
     "-Wno-unused-command-line-argument",
+    # every symbol resolved at link time: a kernel whose host launch stub the
+    # compiler failed to emit is a link error here, not a load error later
+    "-Wl,-z,defs",
 ]
 
 

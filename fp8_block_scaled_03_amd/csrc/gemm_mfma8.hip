@@ -16,14 +16,19 @@
 // gate; these trade that accuracy for the FP8 rate: the FP8 MFMA has twice
 // the FP16 rate and the codes need no widening.
 //
-// Kernel: workgroup tile 256 (i) x 256 (j) x 128 (k), eight waves; wave w
-// owns rows 32w .. 32w+31 and all 256 columns (two 16-row A subtiles x
-// sixteen 16-column B subtiles: 32 MFMAs per block).
+// Kernel: workgroup tile (32 W) (i) x 256 (j) x 128 (k) with W waves: W = 4
+// in the block-scaled modes (128-row tiles, two workgroups per CU, so that
+// one's barrier waits and exposed load latency fall on the other's MFMAs;
+// 3-6% faster than one workgroup of eight waves), W = 8 in the row-scaled
+// mode (wgrad, whose splits are planned for 256x256 tiles and which ran 5%
+// slower in the smaller tile).  Wave w owns rows 32w .. 32w+31 and all 256
+// columns (two 16-row A subtiles x sixteen 16-column B subtiles: 32 MFMAs
+// per block).
 //   A: lane (r16 = l%16, g = l/16) holds codes [32g, 32g+32) of row
 //      32w + 16it + r16 of the block for A subtile it, loaded from global
 //      memory straight into the registers the MFMA reads.
-//   B: the block's 256 x 128 codes are staged in LDS (double buffered; how
-//      they get there is described at the staging code below), in rows of
+//   B: the block's 256 x 128 codes are staged in LDS (double buffered, by
+//      direct global->LDS loads described at the staging code below), in rows of
 //      128 bytes whose 16-byte chunks are XOR-swizzled by bits 1..3 of the
 //      row (lds_off).  Lane (r16, g) reads chunks 2g and 2g+1 of row
 //      16js + r16 as B subtile js's operand: the same K bytes as its A
@@ -43,8 +48,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 
 namespace {
 
-constexpr int kT8 = 256;                      // tile rows and columns
-constexpr int kT8Threads = 512;
+constexpr int kT8 = 256;                      // tile columns
 constexpr int kB8Bytes = kT8 * kRowBytes;     // one block of B codes: 32 KB
 
 // P = sum over one 128-wide block of dec(a[k]) dec(b[k]) for a 16 x 16
@@ -60,12 +64,14 @@ __device__ __forceinline__ v8i as_v8i(const uint4& lo, const uint4& hi) {
 }
 
 template <int MODE, bool OUT_BF16>
-__global__ __launch_bounds__(kT8Threads, 1) void gemm_mfma8_kernel(
+__global__ __launch_bounds__(MODE == kScaleRow ? 512 : 256, MODE == kScaleRow ? 1 : 2) void gemm_mfma8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
     const float* __restrict__ sB, void* __restrict__ C, int64_t I, int64_t J, int64_t Kc,
     int tiles_i, int tiles_j, int p0, int nps, float* __restrict__ Wsp) {
+    constexpr int kW = MODE == kScaleRow ? 8 : 4;         // waves, 32 tile rows each
+    constexpr int kTI = 32 * kW;                          // tile rows
+    static_assert(!OUT_BF16 || kW * 8192 <= kB8Bytes, "BF16 restaging needs 8 KB per wave");
     __shared__ __align__(16) uint8_t Bs[2][kB8Bytes];
-    __shared__ __align__(16) uint8_t Stage[8 * 8192];     // epilogue: 8 KB per wave
     __shared__ __align__(16) float sBs[2][MODE == kScaleRow ? kT8 : 4];   // per-row B scales
 
     const int tid = threadIdx.x;
@@ -75,7 +81,7 @@ __global__ __launch_bounds__(kT8Threads, 1) void gemm_mfma8_kernel(
     const int g = lane >> 4;
     int ti, tj;
     tile_coords(blockIdx.x, tiles_i, tiles_j, &ti, &tj);
-    const int64_t i0 = (int64_t)ti * kT8, j0 = (int64_t)tj * kT8;
+    const int64_t i0 = (int64_t)ti * kTI, j0 = (int64_t)tj * kT8;
     const int nkb_all = (int)(Kc / 128);
     // Only the row-scaled (wgrad) mode is ever split.
     const int kb0 = MODE == kScaleRow ? split_begin(blockIdx.y, p0, nps) : 0;
@@ -91,24 +97,26 @@ __global__ __launch_bounds__(kT8Threads, 1) void gemm_mfma8_kernel(
         a_src[it] = A + row * Kc + 32 * g;
         sa_src[it] = sA + row * nkb_all;
     }
-    // B staging.  Block-scaled modes: lane l of wave w loads bytes
-    // [64h, 64h+64) of tile row 32w + l%32 (h = l/32) of the next block into
-    // registers at the start of a block and stores them into the other LDS
-    // buffer as logical chunks 4h .. 4h+3 of that row (lds_off) in its
-    // middle.  Row-scaled mode (whose per-element scale products leave no
-    // registers for that): direct global->LDS loads, issued at the start of
-    // a block; wave w fills 1 KB pieces 4w .. 4w+3 (rows 8q .. 8q+7 of piece
-    // q, lane l in slot l: row 8q + l/8, physical chunk l%8 holding logical
-    // chunk (l%8) ^ ((row >> 1) & 7)), and waves 0..3 load the scales of rows
-    // 64w + lane.  The compiler then waits for those loads before the
-    // block's first LDS read (it cannot tell the two buffers apart), which
-    // the row-scaled mode accepts.  Rows past J (a half tile) are clamped;
-    // their columns are never stored.
-    constexpr bool kDmaB = MODE == kScaleRow;
-    const uint8_t* bd_src[4];
+    // B staging: direct global->LDS loads (16 bytes per lane), issued at the
+    // start of the previous block into the other buffer.  The block's 32 KB
+    // are 32 pieces of 1 KB; wave w fills pieces P w .. P w + P - 1 (P =
+    // 32 / W; rows 8q .. 8q+7 of piece q, lane l in slot l: row 8q + l/8,
+    // physical chunk l%8 holding logical chunk (l%8) ^ ((row >> 1) & 7)), and
+    // in the row-scaled mode waves 0..3 load the scales of rows 64w + lane.
+    // The compiler waits for those loads before the block's first LDS read
+    // (it cannot tell the two buffers apart), so their latency is only
+    // partly hidden: in the block-scaled modes the other workgroup on the CU
+    // runs meanwhile.  (Staging through registers instead, loaded at the top
+    // of a block and stored in its middle, was the faster form with one
+    // eight-wave workgroup per CU, and spills in the row-scaled mode.)  Rows
+    // past J (a half tile) are clamped; their columns are never stored.
+    constexpr int kPieces = 32 / kW;
+    // (a fixed bound: with a bound that depends on MODE, the host compilation
+    // emits no launch stubs for this kernel template)
+    const uint8_t* bd_src[8];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int row = 8 * (4 * wave + t) + (lane >> 3);
+    for (int t = 0; t < kPieces; ++t) {
+        const int row = 8 * (kPieces * wave + t) + (lane >> 3);
         const int c = (lane & 7) ^ ((row >> 1) & 7);
         bd_src[t] = B + min(j0 + row, J - 1) * Kc + 16 * c;
     }
@@ -117,37 +125,16 @@ __global__ __launch_bounds__(kT8Threads, 1) void gemm_mfma8_kernel(
     auto issue_b = [&](int kb, int buf) __attribute__((always_inline)) {
         const int64_t koff = (int64_t)kb * 128;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < kPieces; ++t)
             __builtin_amdgcn_global_load_lds(bd_src[t] + koff,
-                                             (lds_void*)(&Bs[buf][(4 * wave + t) * 1024]), 16, 0, 0);
-        if (wave < 4)
+                                             (lds_void*)(&Bs[buf][(kPieces * wave + t) * 1024]), 16,
+                                             0, 0);
+        if (MODE == kScaleRow && wave < 4)
             __builtin_amdgcn_global_load_lds(sbd_src + kb, (lds_void*)(&sBs[buf][64 * wave]), 4, 0,
                                              0);
     };
-    const int brow = 32 * wave + (lane & 31);
-    const int bh = lane >> 5;
-    const int64_t bj = min(j0 + brow, J - 1);
-    const uint8_t* b_src = B + bj * Kc + 64 * bh;
     const int64_t jb0 = j0 / 128;
     const int64_t jb1 = min(jb0 + 1, jb_count - 1);
-    uint4 bn[4];              // next block's B codes (block-scaled modes)
-    auto load_b = [&](int kb) __attribute__((always_inline)) {
-        const int64_t koff = (int64_t)kb * 128;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) bn[q] = *reinterpret_cast<const uint4*>(b_src + koff + 16 * q);
-    };
-    // The opaque register dependence (an asm statement stays between the LDS
-    // reads around it) keeps the compiler from hoisting these stores, and
-    // with them the wait for the loads, to the top of the block, where the
-    // codes are still in flight.
-    auto store_b = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            uint4 w = bn[q];
-            asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
-            *reinterpret_cast<uint4*>(&Bs[buf][lds_off(brow, 4 * bh + q)]) = w;
-        }
-    };
     uint4 an[2][2];           // next block's A codes
     float san[2], sbn0 = 0.f, sbn1 = 0.f;
     auto load_a = [&](int kb) __attribute__((always_inline)) {
@@ -175,24 +162,20 @@ __global__ __launch_bounds__(kT8Threads, 1) void gemm_mfma8_kernel(
         for (int js = 0; js < 16; ++js) acc[it][js] = v4f{0.f, 0.f, 0.f, 0.f};
 
     if (nkb > 0) {
-        if constexpr (kDmaB) {
-            issue_b(kb0, 0);
-        } else {
-            load_b(kb0);
-            store_b(0);
-        }
+        issue_b(kb0, 0);
         load_a(kb0);
     }
 
     // Output half h (columns j0 + 128h .. +127, B subtiles 8h .. 8h+7): lane
     // owns C[i][j .. j+3]; split piece y writes its own FP32 slice.  In the
     // block-scaled modes half 0 leaves while the last block's second half is
-    // computed.  BF16 outputs are restaged through this wave's 8 KB of LDS so
-    // that they leave as whole rows in 16-byte stores.
+    // computed.  BF16 outputs are restaged through this wave's 8 KB of the B
+    // buffer the last block does not read (freebuf), so that they leave as
+    // whole rows in 16-byte stores.
     const bool j_full = j0 + kT8 <= J;               // else only the first 128 columns exist
     constexpr bool kEarlyHalf = MODE != kScaleRow;
-    uint8_t* stage = Stage + wave * 8192;
-    auto out_half = [&](auto h_tag) __attribute__((always_inline)) {
+    auto out_half = [&](auto h_tag, int freebuf) __attribute__((always_inline)) {
+        uint8_t* stage = Bs[freebuf] + wave * 8192;
         constexpr int h = decltype(h_tag)::value;
         if (h == 1 && !j_full) return;
         const int64_t jh = j0 + 128 * h;
@@ -241,14 +224,14 @@ __global__ __launch_bounds__(kT8Threads, 1) void gemm_mfma8_kernel(
         }
     };
 
-    // Block k reads buffer k % 2; the next block's B is loaded at its start
-    // and stored into the other buffer in its middle.
+    // Block k reads buffer k % 2; the next block's B is loaded into the other
+    // one from its start.
     auto run_block = [&](int k, auto more_tag) __attribute__((always_inline)) {
         constexpr bool more = decltype(more_tag)::value;
         const int buf = k & 1;
         const uint8_t* Bt = Bs[buf];
         const float* sBt = sBs[buf];
-        if constexpr (kDmaB) wait_global_loads();   // this wave's direct loads of the block
+        wait_global_loads();      // this wave's direct loads of the block
         __syncthreads();          // B of this block is in Bs[buf]; all waves are done with Bs[buf^1]
         v8i a8[2];
 #pragma unroll
@@ -261,12 +244,8 @@ __global__ __launch_bounds__(kT8Threads, 1) void gemm_mfma8_kernel(
         }
         const float sa[2] = {san[0], san[1]};
         if constexpr (more) {
-            if constexpr (kDmaB) {
-                issue_b(kb0 + k + 1, buf ^ 1);
-                load_a(kb0 + k + 1);
-            } else {
-                load_b(kb0 + k + 1);
-            }
+            issue_b(kb0 + k + 1, buf ^ 1);
+            load_a(kb0 + k + 1);
         }
         auto frag = [&](int js) __attribute__((always_inline)) {
             const int row = 16 * js + r16;
@@ -327,31 +306,28 @@ __global__ __launch_bounds__(kT8Threads, 1) void gemm_mfma8_kernel(
 #pragma unroll
                 for (int it = 0; it < 2; ++it) p[jj][it] = mfma8(bq[cur][jj], a8[it]);
             fold(p, jp);
-            if constexpr (more && !kDmaB) {
-                if (jp == 8 / JJ - 1) {          // the middle of the block
-                    store_b(buf ^ 1);          // next block's B, into the free buffer
-                    load_a(kb0 + k + 1);       // its A codes, in flight until the next block
-                }
-            } else if constexpr (!more && kEarlyHalf) {
+            if constexpr (!more && kEarlyHalf) {
                 // columns 0..127 (subtiles 0..7) are final once their last group is folded
-                if (jp == 8 / JJ - 1) out_half(std::integral_constant<int, 0>{});
+                if (jp == 8 / JJ - 1) out_half(std::integral_constant<int, 0>{}, buf ^ 1);
             }
         }
     };
     for (int k = 0; k + 1 < nkb; ++k) run_block(k, std::true_type{});
     if (nkb > 0) run_block(nkb - 1, std::false_type{});
-    if (!kEarlyHalf || nkb == 0) out_half(std::integral_constant<int, 0>{});
-    out_half(std::integral_constant<int, 1>{});
+    const int freebuf = nkb > 0 ? ((nkb - 1) & 1) ^ 1 : 0;
+    if (!kEarlyHalf || nkb == 0) out_half(std::integral_constant<int, 0>{}, freebuf);
+    out_half(std::integral_constant<int, 1>{}, freebuf);
 }
 
 template <int MODE, bool BF16>
 hipError_t launch_mfma8(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB,
                         void* C, int64_t I, int64_t J, int64_t Kc, GemmSplit s, float* Wsp,
                         hipStream_t stream) {
-    const int tiles_i = (int)((I + kT8 - 1) / kT8);
+    constexpr int kW = MODE == kScaleRow ? 8 : 4;
+    const int tiles_i = (int)((I + 32 * kW - 1) / (32 * kW));
     const int tiles_j = (int)((J + kT8 - 1) / kT8);
     return launch(gemm_mfma8_kernel<MODE, BF16>, dim3(tiles_i * tiles_j, s.pieces),
-                  dim3(kT8Threads), stream, A, sA, B, sB, C, I, J, Kc, tiles_i, tiles_j, s.p0,
+                  dim3(64 * kW), stream, A, sA, B, sB, C, I, J, Kc, tiles_i, tiles_j, s.p0,
                   s.nps, Wsp);
 }
 
