@@ -31,9 +31,18 @@ PEAK_F16_TFLOPS = 2500.0       # MI355X dense FP16 / BF16 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
-    "gemm": ["gemm.hip", "gemm_mfma8.hip", "gemm_common.h", "device_common.h", "internal.h"],
+    "gemm": ["gemm.hip", "gemm_common.h", "device_common.h", "internal.h"],
+    "gemm_mfma8": ["gemm_mfma8.hip", "gemm.hip", "gemm_common.h", "device_common.h", "internal.h"],
     "quant": ["quantize.hip", "device_common.h", "internal.h"],
 }
+
+
+def _source_set(kind: str) -> str:
+    """Which sources a kernel kind is built from (the FP8-MFMA GEMMs' split-K
+    reduction lives in gemm.hip)."""
+    if kind.startswith("gemm"):
+        return "gemm_mfma8" if kind.endswith("_mfma8") else "gemm"
+    return "quant"
 
 
 def _code_only(text: str) -> str:
@@ -51,7 +60,7 @@ def source_digest(kind: str) -> str:
     built from: counter records taken on other code are stale."""
     import hashlib
     h = hashlib.sha256()
-    for fn in KERNEL_SOURCES["gemm" if kind.startswith("gemm") else "quant"]:
+    for fn in KERNEL_SOURCES[_source_set(kind)]:
         with open(os.path.join(ROOT, "fp8_block_scaled_03_amd", "csrc", fn), encoding="utf-8") as f:
             h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
