@@ -84,6 +84,8 @@ def kernel_kind(name: str):
     m = re.search(r"gemm_mfma8_kernel<(\d)", name)
     if m:
         return ("gemm_fprop_mfma8", "gemm_dgrad_mfma8", "gemm_wgrad_mfma8")[int(m.group(1))], True
+    if "quant_block_many_kernel" in name:           # a layer's weights in one launch
+        return "quant_block", True
     if "quant_dual_kernel<false>" in name:          # the token-axis-only instance
         return "quant_transposed", True
     for k in ("quant_rowtile", "quant_block", "quant_transposed", "quant_dual"):
@@ -365,17 +367,28 @@ class Plan:
                          ts.data_ptr(), stream),
                         M * C * 4 + M * (C // 128) * 4 + C * (M // 128) * 4))
 
+        import ctypes
+
+        from fp8_block_scaled_03_amd._binding import BlockJob
+        self._jobs = getattr(self, "_jobs", [])      # the job tables must outlive the ops
         for layer in range(cfg.layers):
             W = self.w[layer]
             fwd = [g for g in cfg.gemms if g.kind == "fprop"]
-            for g in fwd:                                # forward
-                (dual if fused else rowtile)(g.a)
+            # the layer's four weights through the block quantizer in one launch
+            jobs = (BlockJob * len(fwd))()
+            wbytes = 0
+            for i, g in enumerate(fwd):
                 w = W[g.b]
                 N, K2 = w.shape
                 wq, wqt, ws = self.wq[g.b]
-                ops.append(("quant_block", L.fp8_quantize_block,
-                            (w.data_ptr(), N, K2, wq.data_ptr(), wqt.data_ptr(), ws.data_ptr(),
-                             stream), N * K2 * 4 + (N // 128) * (K2 // 128) * 4))
+                jobs[i] = BlockJob(w.data_ptr(), N, K2, wq.data_ptr(), wqt.data_ptr(), ws.data_ptr())
+                wbytes += N * K2 * 4 + (N // 128) * (K2 // 128) * 4
+            self._jobs.append(jobs)
+            ops.append(("quant_block", L.fp8_quantize_block_many,
+                        (ctypes.cast(jobs, ctypes.c_void_p), len(fwd), stream), wbytes))
+            for g in fwd:                                # forward
+                (dual if fused else rowtile)(g.a)
+                wq, wqt, ws = self.wq[g.b]
                 q, s = self.rq[g.a]
                 ops.append(("gemm_fprop", fprop,
                             (q.data_ptr(), s.data_ptr(), wq.data_ptr(), ws.data_ptr(),

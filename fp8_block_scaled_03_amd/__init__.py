@@ -14,7 +14,7 @@ from ._binding import (FP8BS_OUT_BF16, FP8BS_OUT_F32, Fp8bsError, bf16_gemm_tn, 
                        fp8_gemm_wgrad, fp8_gemm_wgrad_accumulate, fp8_gemm_wgrad_mfma8,
                        fp8_gemm_wgrad_mfma8_workspace_bytes,
                        fp8_gemm_wgrad_accumulate_workspace_bytes, fp8_gemm_wgrad_noalloc,
-                       fp8_gemm_wgrad_workspace_bytes, fp8_quantize_block,
+                       fp8_gemm_wgrad_workspace_bytes, fp8_quantize_block, fp8_quantize_block_many,
                        fp8_quantize_dual, fp8_quantize_rowtile, fp8_quantize_transposed,
                        fp8_rmsnorm_quantize_dual, fp8_swiglu_backward_quantize_dual,
                        fp8_swiglu_quantize_dual,

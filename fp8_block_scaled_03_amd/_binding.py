@@ -24,6 +24,14 @@ STATUS_NAMES = {0: "FP8BS_OK", 1: "FP8BS_ERR_NULL", 2: "FP8BS_ERR_SHAPE", 3: "FP
 FP8BS_OUT_F32 = 0
 FP8BS_OUT_BF16 = 1
 
+
+
+class BlockJob(ctypes.Structure):
+    """fp8bs_block_job of include/fp8bs.h."""
+    _fields_ = [("w", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("q", ctypes.c_void_p), ("q_t", ctypes.c_void_p), ("s", ctypes.c_void_p)]
+
+
 # Every symbol include/fp8bs.h declares, with (restype, argtypes).
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -33,6 +41,7 @@ SIGNATURES = {
     "fp8_quantize_block": (_INT, [_P, _I64, _I64, _P, _P, _P, _P]),
     "fp8_quantize_transposed": (_INT, [_P, _I64, _I64, _P, _P, _P]),
     "fp8_quantize_dual": (_INT, [_P, _I64, _I64, _P, _P, _P, _P, _P]),
+    "fp8_quantize_block_many": (_INT, [_P, _INT, _P]),
     "fp8_swiglu_quantize_dual": (_INT, [_P, _I64, _I64, _P, _P, _P, _P, _P, _P]),
     "fp8_rmsnorm_quantize_dual": (_INT, [_P, _P, ctypes.c_float, _I64, _I64, _P, _P, _P, _P, _P,
                                          _P, _P]),
@@ -196,6 +205,35 @@ def fp8_quantize_block(w: torch.Tensor, q=None, q_t=None, s=None, with_transpose
     _check("fp8_quantize_block", capi().fp8_quantize_block(
         _ptr(w), N, K, _ptr(q), _ptr(q_t), _ptr(s), _stream(w, stream)))
     return q, q_t, s
+
+
+def fp8_quantize_block_many(ws, with_transpose=True, stream=None):
+    """Several weights w bf16 [N,K] through the block quantizer in one launch
+    (per 16): returns [(q [N,K], q_t [K,N] or None, s [N/128,K/128]), ...].
+    with_transpose: one bool for all weights or one per weight."""
+    ws = list(ws)
+    flags = ([bool(with_transpose)] * len(ws) if isinstance(with_transpose, bool)
+             else [bool(f) for f in with_transpose])
+    if len(flags) != len(ws):
+        raise ValueError("with_transpose: one flag per weight")
+    outs = []
+    jobs = (BlockJob * max(len(ws), 1))()
+    devs = {}
+    for i, (w, t) in enumerate(zip(ws, flags)):
+        N, K = _bf16_input(w, f"w[{i}]")
+        with _alloc_on(stream, w.device):
+            q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+            q_t = torch.empty((K, N), dtype=torch.uint8, device=w.device) if t else None
+            s = torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device)
+        devs[f"w{i}"] = w
+        outs.append((q, q_t, s))
+        jobs[i] = BlockJob(_ptr(w), N, K, _ptr(q), _ptr(q_t), _ptr(s))
+    if not ws:
+        return outs
+    _on_device(**devs)
+    _check("fp8_quantize_block_many", capi().fp8_quantize_block_many(
+        ctypes.cast(jobs, ctypes.c_void_p), len(ws), _stream(ws[0], stream)))
+    return outs
 
 
 def fp8_quantize_transposed(x: torch.Tensor, qt=None, st=None, stream=None):

@@ -130,6 +130,47 @@ fp8bs_status fp8_quantize_block(const uint16_t* w, int64_t N, int64_t K, uint8_t
     return launched(fp8bs::launch_quant_block(w, N, K, q, q_t, s, stream));
 }
 
+static fp8bs_status check_block_job(const fp8bs_block_job& j) {
+    if (!mult128(j.N) || !mult128(j.K)) return FP8BS_ERR_SHAPE;
+    const bool empty = (j.N == 0 || j.K == 0);
+    FP8BS_TRY(check_ptr(j.w, empty, 16));
+    FP8BS_TRY(check_ptr(j.q, empty, 16));
+    FP8BS_TRY(check_ptr(j.s, empty, 4));
+    if (j.q_t && !aligned(j.q_t, 16)) return FP8BS_ERR_ALIGN;
+    return FP8BS_OK;
+}
+
+fp8bs_status fp8_quantize_block_many(const fp8bs_block_job* jobs, int count,
+                                     fp8bs_stream_t stream) {
+    if (count < 0) return FP8BS_ERR_SHAPE;
+    if (count > 0 && !jobs) return FP8BS_ERR_NULL;
+    bool any = false;
+    for (int i = 0; i < count; ++i) {
+        FP8BS_TRY(check_block_job(jobs[i]));
+        any = any || (jobs[i].N > 0 && jobs[i].K > 0);
+    }
+    if (!any) return FP8BS_OK;
+    int cus;
+    FP8BS_TRY(check_device(&cus));
+    fp8bs::BlockJobs batch{};
+    for (int i = 0; i <= count; ++i) {
+        if (i == count || batch.count == fp8bs::kMaxBlockJobs) {
+            if (batch.count > 0) {
+                const fp8bs_status st = launched(fp8bs::launch_quant_block_many(batch, stream));
+                if (st != FP8BS_OK) return st;
+            }
+            batch = fp8bs::BlockJobs{};
+            if (i == count) break;
+        }
+        const fp8bs_block_job& j = jobs[i];
+        if (j.N == 0 || j.K == 0) continue;
+        const int c = batch.count++;
+        batch.job[c] = fp8bs::BlockJob{j.w, j.N, j.K, j.q, j.q_t, j.s};
+        batch.first[c + 1] = batch.first[c] + (j.N / 128) * (j.K / 128);
+    }
+    return FP8BS_OK;
+}
+
 fp8bs_status fp8_quantize_transposed(const uint16_t* x, int64_t M, int64_t C, uint8_t* qt,
                                      float* st, fp8bs_stream_t stream) {
     if (!mult128(M) || !mult128(C)) return FP8BS_ERR_SHAPE;

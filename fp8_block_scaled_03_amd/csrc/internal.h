@@ -38,6 +38,23 @@ hipError_t launch_quant_rowtile(const uint16_t* x, int64_t M, int64_t K, uint8_t
                                 hipStream_t stream);
 hipError_t launch_quant_block(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, uint8_t* q_t,
                               float* s, hipStream_t stream);
+// Up to kMaxBlockJobs weights quantized by one launch (passed by value as a
+// kernel argument); first[j] is the first workgroup of job j, first[count]
+// the total.
+constexpr int kMaxBlockJobs = 16;
+struct BlockJob {
+    const uint16_t* w;
+    int64_t N, K;
+    uint8_t* q;
+    uint8_t* q_t;
+    float* s;
+};
+struct BlockJobs {
+    int count;
+    int64_t first[kMaxBlockJobs + 1];
+    BlockJob job[kMaxBlockJobs];
+};
+hipError_t launch_quant_block_many(const BlockJobs& jobs, hipStream_t stream);
 hipError_t launch_quant_transposed(const uint16_t* x, int64_t M, int64_t C, uint8_t* qt, float* st,
                                    hipStream_t stream);
 hipError_t launch_quant_dual(const uint16_t* x, int64_t M, int64_t C, uint8_t* q, float* s,

@@ -105,16 +105,15 @@ __device__ __forceinline__ void transpose4x4(uint32_t a0, uint32_t a1, uint32_t 
     out[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
 }
 
-__global__ __launch_bounds__(kBlkThreads) void quant_block_kernel(
-    const uint16_t* __restrict__ w, int64_t N, int64_t K, uint8_t* __restrict__ q,
-    uint8_t* __restrict__ q_t, float* __restrict__ s) {
-    __shared__ uint32_t red[kBlkThreads / 64];
-    __shared__ __align__(16) uint32_t tile_t[kTile * kTile / 4];
-    __shared__ ScaleTables tab;
-    load_scale_tables(&tab);
+// Block `blk` (row-major over the N/128 x K/128 blocks) of one weight; the
+// caller provides the LDS and loads the scale tables.
+__device__ __forceinline__ void block_tile(const uint16_t* __restrict__ w, int64_t N, int64_t K,
+                                           uint8_t* __restrict__ q, uint8_t* __restrict__ q_t,
+                                           float* __restrict__ s, int64_t blk, uint32_t* red,
+                                           uint32_t* tile_t, const ScaleTables& tab) {
     const int tid = threadIdx.x;
     const int64_t kb_count = K / kTile;
-    const int64_t bi = blockIdx.x / kb_count, bj = blockIdx.x % kb_count;
+    const int64_t bi = blk / kb_count, bj = blk % kb_count;
     const int64_t n0 = bi * kTile, k0 = bj * kTile;
     const int cc = tid & 15;              // 16-byte chunk of the row: columns 8cc .. 8cc+7
     const int rg = tid >> 4;              // rows 4rg .. 4rg+3 (+64 in the second pass)
@@ -136,7 +135,7 @@ __global__ __launch_bounds__(kBlkThreads) void quant_block_kernel(
     __syncthreads();
     m = max(max(red[0], red[1]), max(red[2], red[3]));
     const TileScale ts = tile_scale(m, &tab);
-    if (tid == 0) s[bi * kb_count + bj] = ts.s;
+    if (tid == 0) s[bi * kb_count + bj] = ts.s;   // (tile_scale reads tab, published by the barrier above)
 
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -171,12 +170,44 @@ __global__ __launch_bounds__(kBlkThreads) void quant_block_kernel(
     }
 }
 
+__global__ __launch_bounds__(kBlkThreads) void quant_block_kernel(
+    const uint16_t* __restrict__ w, int64_t N, int64_t K, uint8_t* __restrict__ q,
+    uint8_t* __restrict__ q_t, float* __restrict__ s) {
+    __shared__ uint32_t red[kBlkThreads / 64];
+    __shared__ __align__(16) uint32_t tile_t[kTile * kTile / 4];
+    __shared__ ScaleTables tab;
+    load_scale_tables(&tab);
+    block_tile(w, N, K, q, q_t, s, blockIdx.x, red, tile_t, tab);
+}
+
+// Several weights in one launch: workgroup b quantizes block b - first[j] of
+// job j, first[j] <= b < first[j + 1].  One launch of all the blocks fills the
+// CUs where a weight alone (256 to 1536 blocks) leaves many idle or in a
+// ragged last round.
+__global__ __launch_bounds__(kBlkThreads) void quant_block_many_kernel(BlockJobs jobs) {
+    __shared__ uint32_t red[kBlkThreads / 64];
+    __shared__ __align__(16) uint32_t tile_t[kTile * kTile / 4];
+    __shared__ ScaleTables tab;
+    load_scale_tables(&tab);
+    const int64_t b = blockIdx.x;
+    int j = 0;
+    while (j + 1 < jobs.count && b >= jobs.first[j + 1]) ++j;
+    const BlockJob& job = jobs.job[j];
+    block_tile(job.w, job.N, job.K, job.q, job.q_t, job.s, b - jobs.first[j], red, tile_t, tab);
+}
+
 hipError_t launch_quant_block(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, uint8_t* q_t,
                               float* s, hipStream_t stream) {
     int64_t blocks = (N / kTile) * (K / kTile);
     if (blocks == 0) return hipSuccess;
     return launch(quant_block_kernel, dim3((unsigned)blocks), dim3(kBlkThreads), stream, w, N, K,
                   q, q_t, s);
+}
+
+hipError_t launch_quant_block_many(const BlockJobs& jobs, hipStream_t stream) {
+    const int64_t blocks = jobs.first[jobs.count];
+    if (blocks == 0) return hipSuccess;
+    return launch(quant_block_many_kernel, dim3((unsigned)blocks), dim3(kBlkThreads), stream, jobs);
 }
 
 // ---------------------------------------------------------------------------

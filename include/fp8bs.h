@@ -100,6 +100,29 @@ fp8bs_status fp8_quantize_block(const uint16_t* w, int64_t N, int64_t K, uint8_t
                                 float* s, fp8bs_stream_t stream);
 
 /*
+ * Several weights through the block quantizer at once, each quantized exactly
+ * as fp8_quantize_block quantizes it (same passage): a training step
+ * quantizes every weight of a layer (or of the model) after the optimizer
+ * step, and one launch over all their 128x128 blocks fills the device where a
+ * single weight's 256-1536 blocks do not.
+ *   jobs   host array of count descriptions (read before the call returns):
+ *          w bf16 [N, K], q u8 [N, K], q_t u8 [K, N] or NULL, s f32 [N/128, K/128]
+ * Every job is checked as fp8_quantize_block checks its arguments before
+ * anything is launched; the first failing check's status is returned and
+ * nothing is written.  Jobs with N or K = 0 are skipped.  One launch per 16
+ * jobs.  count >= 0 (jobs may be NULL when it is 0).
+ */
+typedef struct fp8bs_block_job {
+    const uint16_t* w;
+    int64_t N, K;
+    uint8_t* q;
+    uint8_t* q_t;
+    float* s;
+} fp8bs_block_job;
+fp8bs_status fp8_quantize_block_many(const fp8bs_block_job* jobs, int count,
+                                     fp8bs_stream_t stream);
+
+/*
  * Token-axis (transposed) quantizer for the weight-gradient operands.
  * The weight gradient contracts over tokens, so its operands are quantized in
  * 1x128 tiles of 128 consecutive tokens of one channel: the row-tile

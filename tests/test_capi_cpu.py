@@ -39,7 +39,7 @@ def L():
 
 def test_exports_every_header_symbol(L):
     names = header_functions()
-    assert len(names) == 25, names
+    assert len(names) == 26, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -75,6 +75,21 @@ def test_quantizer_argument_errors(L):
     assert L.fp8_quantize_block(A16, 128, 128, None, None, A16, None) == NULL
     assert L.fp8_quantize_block(A16, 128, 128, A16, MIS, A16, None) == ALIGN
     assert L.fp8_quantize_block(None, 0, 128, None, None, None, None) == OK
+
+    # several weights in one call: every job is checked before anything runs
+    J = B.BlockJob
+    def many(*jobs):
+        arr = (J * max(len(jobs), 1))(*jobs)
+        return L.fp8_quantize_block_many(ctypes.cast(arr, ctypes.c_void_p), len(jobs), None)
+    good = J(A16, 128, 256, A16, None, A16)
+    assert L.fp8_quantize_block_many(None, -1, None) == SHAPE
+    assert L.fp8_quantize_block_many(None, 1, None) == NULL
+    assert L.fp8_quantize_block_many(None, 0, None) == OK
+    assert many(good, J(A16, 100, 128, A16, None, A16)) == SHAPE
+    assert many(good, J(A16, 128, 128, None, None, A16)) == NULL
+    assert many(J(A16, 128, 128, A16, MIS, A16), good) == ALIGN
+    assert many(good, J(A16, 128, 128, A16, None, A16 + 2)) == ALIGN
+    assert many(J(None, 0, 128, None, None, None), J(None, 256, 0, None, None, None)) == OK
 
     assert L.fp8_quantize_transposed(A16, 100, 128, A16, A16, None) == SHAPE
     assert L.fp8_quantize_transposed(A16, 128, 96, A16, A16, None) == SHAPE
@@ -309,6 +324,8 @@ def test_binding_rejects_mismatched_inputs_before_any_call(monkeypatch):
         ("h", lambda: B.fp8_swiglu_quantize_dual(E((256, 256), bf), h=E((256, 256), bf))),
         ("qt", lambda: B.fp8_swiglu_quantize_dual(E((256, 256), bf), qt=E((256, 128), u8))),
         ("gate_up", lambda: B.fp8_swiglu_backward_quantize_dual(E((256, 128), bf), E((256, 128), bf))),
+        ("w\\[1\\]", lambda: B.fp8_quantize_block_many([E((128, 128), bf), E((128, 128), f32)])),
+        ("one flag", lambda: B.fp8_quantize_block_many([E((128, 128), bf)], with_transpose=[True, False])),
         ("gamma", lambda: B.fp8_rmsnorm_quantize_dual(E((256, 128), bf), E((256,), bf))),
         ("gamma", lambda: B.fp8_rmsnorm_quantize_dual(E((256, 128), bf), E((128,), f32))),
         ("rstd", lambda: B.fp8_rmsnorm_quantize_dual(E((256, 128), bf), E((128,), bf),
