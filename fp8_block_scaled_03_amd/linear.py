@@ -146,7 +146,8 @@ class Fp8SwiGLUMLPFunction(torch.autograd.Function):
     the SwiGLU's output (forward) and input gradient (backward) quantized on
     produce.
 
-    forward   X -> fp8_quantize_dual; GU = fprop(X, W_gu) in BF16 [T, 2F]
+    forward   W_gu, W_down -> fp8_quantize_block_many (one launch);
+              X -> fp8_quantize_dual; GU = fprop(X, W_gu) in BF16 [T, 2F]
               (gate | up); fp8_swiglu_quantize_dual(GU) -> H's row tiles (the
               down projection's fprop) and token-axis tiles (its wgrad);
               Y = fprop(H, W_down).  GU is kept for the backward; H is never
@@ -172,11 +173,10 @@ class Fp8SwiGLUMLPFunction(torch.autograd.Function):
         _check_dims(x2d.shape[0], x2d.shape[1], 2 * F)
         _check_dims(x2d.shape[0], F, x2d.shape[1])
         fprop = B.fp8_gemm_fprop_mfma8 if mfma8 else B.fp8_gemm_fprop
+        (gq, gqt, gs), (dq, dqt, dsc) = B.fp8_quantize_block_many([wgu, wd])   # one launch
         xq, xs, xtq, xts = B.fp8_quantize_dual(x2d)
-        gq, gqt, gs = B.fp8_quantize_block(wgu, with_transpose=True)
         gu = fprop(xq, xs, gq, gs, out_dtype=torch.bfloat16)
         hq, hs, htq, hts, _ = B.fp8_swiglu_quantize_dual(gu)
-        dq, dqt, dsc = B.fp8_quantize_block(wd, with_transpose=True)
         y = fprop(hq, hs, dq, dsc, out_dtype=torch.bfloat16)
         ctx.save_for_backward(xtq, xts, gqt, gs, gu, htq, hts, dqt, dsc)
         ctx.weights = (w_gu, w_down)

@@ -28,22 +28,33 @@ def test_quantizers_run_on_the_callers_stream():
     M, C = 256, 512
     old = to_dev_bf16(inputs.normal((40,), (M, C)))
     new = to_dev_bf16(inputs.student_t((41,), (M, C), 3.0, 0.5))
-    x = old.clone()
+    old_dh = to_dev_bf16(inputs.normal((45,), (M, C // 2)))
+    new_dh = to_dev_bf16(inputs.normal((46,), (M, C // 2), 0.5))
+    gamma = to_dev_bf16(inputs.normal((47,), (C,), 0.5))
+    x, dh = old.clone(), old_dh.clone()
     side = torch.cuda.Stream()
     torch.cuda.synchronize()
-    print("quantizers on a side stream", flush=True)
+    print("quantizers and quantize-on-produce calls on a side stream", flush=True)
+
+    def calls(x, dh):
+        return (fp8.fp8_quantize_rowtile(x), fp8.fp8_quantize_dual(x),
+                fp8.fp8_quantize_transposed(x), fp8.fp8_quantize_block(x),
+                fp8.fp8_quantize_block_many([x, dh])[1],
+                fp8.fp8_rmsnorm_quantize_dual(x, gamma, 1e-6, with_y=True),
+                fp8.fp8_swiglu_quantize_dual(x, with_h=True),
+                fp8.fp8_swiglu_backward_quantize_dual(dh, x, with_bf16=True))
+
     with torch.cuda.stream(side):
         torch.cuda._sleep(SPIN_CYCLES)
         x.copy_(new)
-        got = (fp8.fp8_quantize_rowtile(x), fp8.fp8_quantize_dual(x),
-               fp8.fp8_quantize_transposed(x), fp8.fp8_quantize_block(x))
+        dh.copy_(new_dh)
+        got = calls(x, dh)
     side.synchronize()
-    want = (fp8.fp8_quantize_rowtile(new), fp8.fp8_quantize_dual(new),
-            fp8.fp8_quantize_transposed(new), fp8.fp8_quantize_block(new))
+    want = calls(new, new_dh)
     torch.cuda.synchronize()
     for g, w in zip(got, want):
         for a, b in zip(g, w):
-            assert _same(a, b)
+            assert (a is None and b is None) or _same(a, b)
 
 
 def test_gemms_run_on_the_callers_stream():
