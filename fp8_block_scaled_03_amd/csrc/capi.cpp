@@ -86,7 +86,7 @@ int enum_value(const E& e) {
 
 extern "C" {
 
-int fp8bs_version(void) { return 200; }
+int fp8bs_version(void) { return 300; }
 
 const char* fp8bs_status_string(fp8bs_status status) {
     switch (enum_value(status)) {

@@ -16,6 +16,10 @@
  *   - each GEMM sums, per 128-wide contraction block, the FP8 products in
  *     FP32 and folds that partial sum into an FP32 accumulator multiplied by
  *     the two operands' scales for the block.  Outputs are BF16 or FP32.
+ * Beside the quantizers and GEMMs, the BF16 ops that produce linear-layer
+ * operands in a decoder (RMSNorm, the MLP's SwiGLU and its backward) are
+ * offered with their outputs quantized on produce, and several weights can
+ * go through the block quantizer in one launch.
  *
  * Conventions shared by every call:
  *   - Every tensor pointer is a device pointer on the current HIP device,

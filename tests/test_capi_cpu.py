@@ -46,7 +46,7 @@ def test_exports_every_header_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.fp8bs_version() == 200
+    assert L.fp8bs_version() == 300
     for st in range(9):
         s = L.fp8bs_status_string(st)
         assert s and isinstance(s, bytes)
