@@ -68,7 +68,13 @@ fp8bs_status check_ptr(const void* p, bool empty, size_t align) {
         if (st_ != FP8BS_OK) return st_;     \
     } while (0)
 
-fp8bs_status launched(hipError_t e) { return e == hipSuccess ? FP8BS_OK : FP8BS_ERR_HIP; }
+// A launch refused for its size (more work-items along a grid dimension than
+// one dispatch holds; nothing was enqueued) is a shape error; any other
+// failure is the runtime's.
+fp8bs_status launched(hipError_t e) {
+    if (e == hipSuccess) return FP8BS_OK;
+    return e == hipErrorInvalidConfiguration ? FP8BS_ERR_SHAPE : FP8BS_ERR_HIP;
+}
 
 // The integer a caller passed for an enum parameter.  A C caller may pass any
 // int there; in C++ an enum object holding a value outside its enumerators'

@@ -706,7 +706,7 @@ static hipError_t launch_small(const uint8_t* A, const float* sA, const uint8_t*
     int64_t tiles_j = J / kBN;
     int64_t blocks = tiles_i * tiles_j;
     if (blocks == 0) return hipSuccess;
-    return launch(gemm_bs_fp8_kernel<MODE, BF16, ACC>, dim3((unsigned)blocks, pieces), dim3(kThreads),
+    return launch(gemm_bs_fp8_kernel<MODE, BF16, ACC>, dim3(grid1d(blocks).x, pieces), dim3(kThreads),
                   stream, A, sA, B, sB, C, I, J, Kc, (int)tiles_i, (int)tiles_j, p0, nps, Wsp);
 }
 
@@ -837,7 +837,7 @@ hipError_t launch_splitk_reduce(const float* ws, float* out, int64_t n, int slic
                                hipStream_t stream) {
     const int64_t n4 = n / 4;
     if (n4 == 0 || slices <= 0) return hipSuccess;
-    return launch(splitk_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), stream,
+    return launch(splitk_reduce_kernel, grid1d((n4 + 255) / 256), dim3(256), stream,
                   reinterpret_cast<const float4*>(ws), reinterpret_cast<float4*>(out), n4,
                   slices);
 }
@@ -875,7 +875,7 @@ static hipError_t launch_mode(const uint8_t* A, const float* sA, const uint8_t* 
                                               Wsp, stream);
     if (e != hipSuccess || p.pieces <= 1) return e;
     const int64_t n4 = I * J / 4;
-    return launch(splitk_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), stream,
+    return launch(splitk_reduce_kernel, grid1d((n4 + 255) / 256), dim3(256), stream,
                   reinterpret_cast<const float4*>(Wsp), reinterpret_cast<float4*>(C), n4,
                   p.pieces - 1);
 }
@@ -910,7 +910,7 @@ hipError_t launch_wgrad_accumulate(const uint8_t* A, const float* sA, const uint
                                                S + I * J, stream);
     if (e != hipSuccess) return e;
     const int64_t n4 = I * J / 4;
-    return launch(splitk_reduce_acc_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), stream,
+    return launch(splitk_reduce_acc_kernel, grid1d((n4 + 255) / 256), dim3(256), stream,
                   reinterpret_cast<const float4*>(S), reinterpret_cast<float4*>(C), n4, p.pieces);
 }
 
@@ -979,7 +979,7 @@ __global__ __launch_bounds__(256) void mfma_rate_kernel(float* __restrict__ out,
 
 hipError_t launch_mfma_rate(float* out, int64_t blocks, int iters, float v, hipStream_t stream) {
     if (blocks == 0) return hipSuccess;
-    return launch(mfma_rate_kernel, dim3((unsigned)blocks), dim3(256), stream, out, iters, v);
+    return launch(mfma_rate_kernel, grid1d(blocks), dim3(256), stream, out, iters, v);
 }
 
 }  // namespace fp8bs

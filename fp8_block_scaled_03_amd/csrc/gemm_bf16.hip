@@ -174,9 +174,9 @@ hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* B, void* C, bool 
     const int64_t blocks = tiles_i * tiles_j;
     if (blocks == 0) return hipSuccess;
     if (out_bf16)
-        return launch(gemm_bf16_kernel<true>, dim3((unsigned)blocks), dim3(kB16Threads), stream, A,
+        return launch(gemm_bf16_kernel<true>, grid1d(blocks), dim3(kB16Threads), stream, A,
                       B, C, I, J, K, (int)tiles_i, (int)tiles_j);
-    return launch(gemm_bf16_kernel<false>, dim3((unsigned)blocks), dim3(kB16Threads), stream, A, B,
+    return launch(gemm_bf16_kernel<false>, grid1d(blocks), dim3(kB16Threads), stream, A, B,
                   C, I, J, K, (int)tiles_i, (int)tiles_j);
 }
 

@@ -9,15 +9,31 @@
 
 namespace fp8bs {
 
+// A grid dimension covers at most 2^32 - 1 work-items (the HSA dispatch
+// packet's grid size is a 32-bit count of work-items, not of workgroups).
+constexpr uint64_t kMaxGridItems = 0xFFFFFFFFull;
+
+// A one-dimensional grid of `blocks` workgroups.  A count past what a dim3
+// holds saturates, so that launch() rejects it instead of a truncated grid
+// running part of the work.
+inline dim3 grid1d(int64_t blocks) {
+    return dim3(blocks > (int64_t)kMaxGridItems ? (unsigned)kMaxGridItems : (unsigned)blocks);
+}
+
 // Launch kernel k on stream with the given arguments (converted to the
 // kernel's parameter types) and return the status of this launch alone:
 // hipLaunchKernel reports its own failure directly, so an error left behind
 // by an earlier, unrelated HIP call on this thread is never returned (nor
-// cleared) here.
+// cleared) here.  A grid with more than kMaxGridItems work-items along a
+// dimension is refused with hipErrorInvalidConfiguration before anything is
+// enqueued.
 template <typename... KArgs, typename... Args>
 inline hipError_t launch(void (*k)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
                          Args... args) {
     static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
+    if ((uint64_t)grid.x * block.x > kMaxGridItems || (uint64_t)grid.y * block.y > kMaxGridItems ||
+        (uint64_t)grid.z * block.z > kMaxGridItems)
+        return hipErrorInvalidConfiguration;
     std::tuple<KArgs...> values(args...);
     return std::apply(
         [&](auto&... v) {

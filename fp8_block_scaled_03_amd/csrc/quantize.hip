@@ -10,6 +10,8 @@
 // the amax is reduced across the lanes that share a tile, and the codes are
 // produced by the packed FP32 -> E4M3 conversion instruction.  The per-tile
 // divisions are table lookups (see tile_scale in device_common.h).
+#include <algorithm>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -67,7 +69,7 @@ hipError_t launch_quant_rowtile(const uint16_t* x, int64_t M, int64_t K, uint8_t
     int64_t ntiles = M * (K / kTile);
     if (ntiles == 0) return hipSuccess;
     int64_t blocks = (ntiles + kRowTilesPerBlock - 1) / kRowTilesPerBlock;
-    return launch(quant_rowtile_kernel, dim3((unsigned)blocks), dim3(kRowThreads), stream,
+    return launch(quant_rowtile_kernel, grid1d(blocks), dim3(kRowThreads), stream,
                   reinterpret_cast<const uint4*>(x), reinterpret_cast<uint2*>(q), s, ntiles);
 }
 
@@ -200,14 +202,14 @@ hipError_t launch_quant_block(const uint16_t* w, int64_t N, int64_t K, uint8_t* 
                               float* s, hipStream_t stream) {
     int64_t blocks = (N / kTile) * (K / kTile);
     if (blocks == 0) return hipSuccess;
-    return launch(quant_block_kernel, dim3((unsigned)blocks), dim3(kBlkThreads), stream, w, N, K,
+    return launch(quant_block_kernel, grid1d(blocks), dim3(kBlkThreads), stream, w, N, K,
                   q, q_t, s);
 }
 
 hipError_t launch_quant_block_many(const BlockJobs& jobs, hipStream_t stream) {
     const int64_t blocks = jobs.first[jobs.count];
     if (blocks == 0) return hipSuccess;
-    return launch(quant_block_many_kernel, dim3((unsigned)blocks), dim3(kBlkThreads), stream, jobs);
+    return launch(quant_block_many_kernel, grid1d(blocks), dim3(kBlkThreads), stream, jobs);
 }
 
 // ---------------------------------------------------------------------------
@@ -498,27 +500,32 @@ __global__ __launch_bounds__(kDualThreads) void swiglu_bwd_dual_kernel(
 // summing the squares of its 16-byte pieces (columns 8l, 8l + 512, ...) in
 // FP32, then a butterfly over the wave; correctly rounded square root and
 // division.  Four rows per 256-thread workgroup.
+constexpr int64_t kRstdMaxBlocks = 1 << 20;   // 4M rows per pass of the grid
+
 __global__ __launch_bounds__(256) void rmsnorm_rstd_kernel(const uint16_t* __restrict__ x,
                                                            int64_t M, int64_t C, float eps,
                                                            float* __restrict__ rstd) {
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= M) return;
-    const uint16_t* xr = x + row * C;
-    float ss = 0.f;
-    for (int64_t c = 8 * lane; c < C; c += 512) {
-        const uint4 v = load_stream16(xr + c);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    // One wave per row; the grid is capped (kRstdMaxBlocks), so a wave may
+    // take several rows, gridDim.x * 4 apart.
+    for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < M;
+         row += (int64_t)gridDim.x * 4) {
+        const uint16_t* xr = x + row * C;
+        float ss = 0.f;
+        for (int64_t c = 8 * lane; c < C; c += 512) {
+            const uint4 v = load_stream16(xr + c);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float a = bf16_lo(w[j]), b = bf16_hi(w[j]);
-            ss = __builtin_fmaf(a, a, ss);
-            ss = __builtin_fmaf(b, b, ss);
+            for (int j = 0; j < 4; ++j) {
+                const float a = bf16_lo(w[j]), b = bf16_hi(w[j]);
+                ss = __builtin_fmaf(a, a, ss);
+                ss = __builtin_fmaf(b, b, ss);
+            }
         }
-    }
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) ss += __shfl_xor(ss, o);
-    if (lane == 0) rstd[row] = 1.0f / sqrtf(ss / (float)C + eps);
+        for (int o = 1; o < 64; o <<= 1) ss += __shfl_xor(ss, o);
+        if (lane == 0) rstd[row] = 1.0f / sqrtf(ss / (float)C + eps);
+    }
 }
 
 __global__ __launch_bounds__(kDualThreads) void rmsnorm_dual_kernel(
@@ -538,11 +545,16 @@ hipError_t launch_rmsnorm_dual(const uint16_t* x, const uint16_t* gamma, float e
                                int64_t C, uint8_t* q, float* s, uint8_t* qt, float* st,
                                float* rstd, uint16_t* y, hipStream_t stream) {
     if (M == 0 || C == 0) return hipSuccess;
-    hipError_t e = launch(rmsnorm_rstd_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), stream, x,
-                          M, C, eps, rstd);
+    // The dual kernel's grid is checked first, so that a refused call
+    // enqueues nothing.
+    const int64_t tiles = (M / kTile) * (C / kTile);
+    if ((uint64_t)tiles * kDualThreads > kMaxGridItems) return hipErrorInvalidConfiguration;
+    const int64_t rstd_blocks = std::min<int64_t>((M + 3) / 4, kRstdMaxBlocks);
+    hipError_t e = launch(rmsnorm_rstd_kernel, grid1d(rstd_blocks), dim3(256), stream, x, M, C, eps,
+                          rstd);
     if (e != hipSuccess) return e;
-    return launch(rmsnorm_dual_kernel, dim3((unsigned)((M / kTile) * (C / kTile))),
-                  dim3(kDualThreads), stream, x, gamma, (const float*)rstd, M, C, q, s, qt, st, y);
+    return launch(rmsnorm_dual_kernel, grid1d(tiles), dim3(kDualThreads), stream, x, gamma,
+                  (const float*)rstd, M, C, q, s, qt, st, y);
 }
 
 hipError_t launch_swiglu_bwd_dual(const uint16_t* dh, const uint16_t* gu, int64_t M, int64_t F,
@@ -550,7 +562,7 @@ hipError_t launch_swiglu_bwd_dual(const uint16_t* dh, const uint16_t* gu, int64_
                                   hipStream_t stream) {
     int64_t blocks = (M / kTile) * (F / kTile);
     if (blocks == 0) return hipSuccess;
-    return launch(swiglu_bwd_dual_kernel, dim3((unsigned)blocks), dim3(kDualThreads), stream, dh,
+    return launch(swiglu_bwd_dual_kernel, grid1d(blocks), dim3(kDualThreads), stream, dh,
                   gu, M, F, q, s, qt, st, dgu);
 }
 
@@ -558,7 +570,7 @@ hipError_t launch_swiglu_dual(const uint16_t* gu, int64_t M, int64_t F, uint8_t*
                               uint8_t* qt, float* st, uint16_t* h, hipStream_t stream) {
     int64_t blocks = (M / kTile) * (F / kTile);
     if (blocks == 0) return hipSuccess;
-    return launch(swiglu_dual_kernel, dim3((unsigned)blocks), dim3(kDualThreads), stream, gu, M, F,
+    return launch(swiglu_dual_kernel, grid1d(blocks), dim3(kDualThreads), stream, gu, M, F,
                   q, s, qt, st, h);
 }
 
@@ -566,7 +578,7 @@ hipError_t launch_quant_transposed(const uint16_t* x, int64_t M, int64_t C, uint
                                    hipStream_t stream) {
     int64_t blocks = (M / kTile) * (C / kTile);
     if (blocks == 0) return hipSuccess;
-    return launch(quant_dual_kernel<false>, dim3((unsigned)blocks), dim3(kDualThreads), stream, x,
+    return launch(quant_dual_kernel<false>, grid1d(blocks), dim3(kDualThreads), stream, x,
                   M, C, (uint8_t*)nullptr, (float*)nullptr, qt, st);
 }
 
@@ -574,7 +586,7 @@ hipError_t launch_quant_dual(const uint16_t* x, int64_t M, int64_t C, uint8_t* q
                              uint8_t* qt, float* st, hipStream_t stream) {
     int64_t blocks = (M / kTile) * (C / kTile);
     if (blocks == 0) return hipSuccess;
-    return launch(quant_dual_kernel<true>, dim3((unsigned)blocks), dim3(kDualThreads), stream, x, M,
+    return launch(quant_dual_kernel<true>, grid1d(blocks), dim3(kDualThreads), stream, x, M,
                   C, q, s, qt, st);
 }
 
@@ -597,7 +609,7 @@ __global__ __launch_bounds__(256) void encode_e4m3_kernel(const float* __restric
 hipError_t launch_encode_e4m3(const float* x, int64_t n, uint8_t* q, hipStream_t stream) {
     if (n == 0) return hipSuccess;
     int64_t blocks = (n + 1023) / 1024;
-    return launch(encode_e4m3_kernel, dim3((unsigned)blocks), dim3(256), stream, x, n, q);
+    return launch(encode_e4m3_kernel, grid1d(blocks), dim3(256), stream, x, n, q);
 }
 
 // ---------------------------------------------------------------------------
@@ -635,7 +647,7 @@ hipError_t launch_hbm_rate(const uint16_t* x, int64_t n, uint8_t* y0, uint8_t* y
                            hipStream_t stream) {
     if (n == 0) return hipSuccess;
     const int64_t blocks = (n + 4095) / 4096;
-    return launch(hbm_rate_kernel, dim3((unsigned)blocks), dim3(256), stream, x, n, y0, y1);
+    return launch(hbm_rate_kernel, grid1d(blocks), dim3(256), stream, x, n, y0, y1);
 }
 
 }  // namespace fp8bs

@@ -32,7 +32,11 @@
  *     reached the call.
  *   - Errors: argument errors are detected before anything is enqueued; the
  *     call then returns the status and leaves every output untouched.  A
- *     failed launch returns FP8BS_ERR_HIP.  Faults inside a kernel surface at
+ *     failed launch returns FP8BS_ERR_HIP.  Sizes so large that one kernel
+ *     launch would need more than 2^32 - 1 work-items along a grid dimension
+ *     are refused with FP8BS_ERR_SHAPE before anything is enqueued; with
+ *     buffers that fit in device memory only the diagnostics
+ *     (fp8_encode_e4m3, fp8bs_hbm_rate, fp8bs_mfma_rate) can reach that.  Faults inside a kernel surface at
  *     the caller's next synchronization of the stream.  Inputs must be finite;
  *     the library does not check this (a non-finite input gives unspecified
  *     codes for its tile).

@@ -48,3 +48,20 @@ def test_hbm_rate_kernel_moves_the_bytes(n):
     assert torch.equal(y0.to(torch.int32), u >> 8)
     assert torch.equal(y1.to(torch.int32), u & 0xFF)
     assert z1 is None and torch.equal(z0, y0)
+
+
+def test_launch_past_the_grid_limit_is_a_shape_error():
+    """2^24 + 1 workgroups of 256 threads need more than 2^32 - 1 work-items
+    in one grid dimension: the call is refused with FP8BS_ERR_SHAPE before
+    anything is enqueued.  The output buffer is still sized for the whole
+    grid (16 GiB), so that even a launch would stay inside it."""
+    blocks = (1 << 24) + 1
+    out = torch.full((blocks * 256,), -1.0, dtype=torch.float32, device="cuda")
+    print(f"mfma_rate refused blocks={blocks}", flush=True)
+    with pytest.raises(fp8.Fp8bsError) as err:
+        fp8.fp8bs_mfma_rate(blocks, 0, out=out)
+    torch.cuda.synchronize()
+    assert err.value.status == 2
+    assert bool((out[:1024] == -1.0).all()) and bool((out[-1024:] == -1.0).all())
+    del out
+    torch.cuda.empty_cache()

@@ -105,3 +105,41 @@ def test_rmsnorm_dual_qkv_input_size():
     g = next(g for g in c.gemms if g.kind == "fprop")
     x = inputs.tensor("qkv", g.a)
     _check(x, _gamma(x.shape[1], 134), 1e-6, "rmsnorm qkv input")
+
+
+def test_rmsnorm_dual_rows_past_one_grid_pass():
+    """4,194,688 rows of 128 channels: the per-row 1/RMS kernel runs a capped
+    grid of 2^20 workgroups (4 rows each), so rows past 2^22 are taken on a
+    second pass.  Row m holds row (7919 m) mod 8192 of a seeded base (a
+    permutation of every 8192-row window): r is compared on every row, Y and
+    the row-tile codes on 12,288 rows (first, last, random), the token-axis
+    codes on the 128-row blocks around 2^22 and at the end."""
+    M, C, B = (1 << 22) + 384, 128, 8192
+    base = inputs.normal((135, B, C), (B, C), 1.0)
+    g_bits = _gamma(C, 136)
+    idx = (np.arange(M, dtype=np.int64) * 7919) % B
+    x = to_dev_bf16(base)[torch.from_numpy(idx).cuda()]
+    gamma = to_dev_bf16(g_bits)
+    _say(f"rmsnorm {M}x{C} (two grid passes)")
+    q, s, qt, st, r, y = fp8.fp8_rmsnorm_quantize_dual(x, gamma, 1e-6, with_y=True)
+    torch.cuda.synchronize()
+    yo, ro = oracle.rmsnorm(base, g_bits, 1e-6)
+    rk = to_np(r).astype(np.float64)
+    assert float(np.max(np.abs(rk - ro[idx]) / ro[idx])) <= 2.0 ** -20
+    rng = np.random.default_rng(137)
+    rows = np.unique(np.concatenate([np.arange(4096), np.arange(M - 4096, M),
+                                     rng.integers(0, M, 4096)]))
+    rows_t = torch.from_numpy(rows).cuda()
+    yk = to_np(y[rows_t])
+    want = bf16_to_f64(yo[idx[rows]])
+    assert np.all(np.abs(bf16_to_f64(yk) - want) <= bf16_ulp(want))
+    oq, os_ = oracle.quantize_rowtile(yk)
+    assert np.array_equal(to_np(q[rows_t]), oq)
+    assert np.array_equal(to_np(s[rows_t]).view(np.uint32), os_.view(np.uint32))
+    for mb in ((1 << 22) // 128 - 1, (1 << 22) // 128, M // 128 - 1):
+        yb = to_np(y[128 * mb:128 * (mb + 1)])
+        oqt, ost = oracle.quantize_transposed(yb)
+        assert np.array_equal(to_np(qt[:, 128 * mb:128 * (mb + 1)]), oqt), f"qt block {mb}"
+        assert np.array_equal(to_np(st[:, mb:mb + 1]).view(np.uint32), ost.view(np.uint32))
+    del x, q, s, qt, st, r, y
+    torch.cuda.empty_cache()
