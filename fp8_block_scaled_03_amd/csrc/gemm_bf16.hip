@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kB16Threads, 1) void gemm_bf16_kernel(
     const uint8_t* a_bytes = reinterpret_cast<const uint8_t*>(A);
     const uint8_t* b_bytes = reinterpret_cast<const uint8_t*>(B);
     const int prow = 64 * (wave & 3) + (lane >> 3);
-    const int pc = (lane & 7) ^ ((prow >> 1) & 7);
+    const int pc = (lane & 7) ^ lds_swz_bf16(prow);
     auto issue_loads = [&](int ks, int buf) {
         if (wave >= 4) return;
         const int64_t koff = (int64_t)ks * kRowBytes;
@@ -95,7 +95,8 @@ __global__ __launch_bounds__(kB16Threads, 1) void gemm_bf16_kernel(
             const int row = wi * 64 + it * 16 + r16;
 #pragma unroll
             for (int c = 0; c < 2; ++c)
-                af[it][c] = *reinterpret_cast<const v8bf*>(At + lds_off(row, 4 * c + g));
+                af[it][c] =
+                    *reinterpret_cast<const v8bf*>(At + lds_off(row, 4 * c + g, lds_swz_bf16(row)));
         }
 #pragma unroll
         for (int js = 0; js < 8; ++js) {
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(kB16Threads, 1) void gemm_bf16_kernel(
             v8bf bf[2];
 #pragma unroll
             for (int c = 0; c < 2; ++c)
-                bf[c] = *reinterpret_cast<const v8bf*>(Bt + lds_off(row, 4 * c + g));
+                bf[c] = *reinterpret_cast<const v8bf*>(Bt + lds_off(row, 4 * c + g, lds_swz_bf16(row)));
 #pragma unroll
             for (int c = 0; c < 2; ++c)
 #pragma unroll

@@ -14,12 +14,25 @@ constexpr int kRowBytes = 128;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Byte offset of 16-byte chunk c (0..7, K = 16c .. 16c+15) of tile row r.  The
-// chunk index is XORed with bits 1..3 of the row, so that the 16 lanes served
-// together by a 16-byte LDS read (16 consecutive rows, one logical chunk)
-// cover all 64 banks exactly once.
-__device__ __forceinline__ int lds_off(int row, int c) {
-    return row * kRowBytes + ((c ^ ((row >> 1) & 7)) << 4);
+// Row r's 16-byte chunk c (0..7, K = 16c .. 16c+15) is stored at physical
+// chunk c ^ swz(r).  A fragment read takes one logical chunk per lane group
+// g = lane / 16 from 16 consecutive rows (lanes r16 = lane % 16).  Which row
+// swizzle keeps those reads free of LDS bank conflicts depends on the chunks
+// the four lane groups read; both swizzles below were chosen by rocprofv3's
+// LDS bank-conflict counter (conflict cycles over LDS-active cycles):
+//   lds_swz_fp8   rows' bits 0..2, bit 3 flipping the lowest: for reads in
+//                 which group g takes chunks 2g and 2g+1 (the FP8 tiles of
+//                 the FP8-MFMA and the 128x128 kernels): 0-5%, against
+//                 46-49% with lds_swz_bf16;
+//   lds_swz_bf16  rows' bits 1..3: for reads in which group g takes chunk g
+//                 or 4+g (the BF16 comparator's tiles): 3%, against 50% with
+//                 lds_swz_fp8.
+__device__ __forceinline__ int lds_swz_fp8(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int lds_swz_bf16(int row) { return (row >> 1) & 7; }
+
+// Byte offset of 16-byte chunk c of tile row `row` under row swizzle swz.
+__device__ __forceinline__ int lds_off(int row, int c, int swz) {
+    return row * kRowBytes + ((c ^ swz) << 4);
 }
 
 // vmcnt(0): this wave's global loads (including those into LDS) have landed.

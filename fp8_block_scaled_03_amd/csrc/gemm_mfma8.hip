@@ -29,12 +29,11 @@
 //      memory straight into the registers the MFMA reads.
 //   B: the block's 256 x 128 codes are staged in LDS (double buffered, by
 //      direct global->LDS loads described at the staging code below), in rows of
-//      128 bytes whose 16-byte chunks are XOR-swizzled by bits 1..3 of the
-//      row (lds_off).  Lane (r16, g) reads chunks 2g and 2g+1 of row
-//      16js + r16 as B subtile js's operand: the same K bytes as its A
-//      operand, so each lane pairs A and B codes of the same K and the
-//      instruction sums the whole block.  The 16 lanes served by one 16-byte
-//      LDS read cover all banks once.
+//      128 bytes whose 16-byte chunks are XOR-swizzled by row (lds_swz_fp8).
+//      Lane (r16, g) reads chunks 2g and 2g+1 of row 16js + r16 as B
+//      subtile js's operand: the same K bytes as its A operand, so each lane
+//      pairs A and B codes of the same K and the instruction sums the whole
+//      block.  Those reads are free of bank conflicts.
 //   Output: the MFMA is issued as (B, A), so lane (r16, g) holds columns
 //      16js + 4g .. +3 of row 16it + r16 -- the layout of gemm.hip's 256x256
 //      kernel, whose fold and epilogue this kernel repeats.
@@ -101,7 +100,7 @@ __global__ __launch_bounds__(MODE == kScaleRow ? 512 : 256, MODE == kScaleRow ? 
     // start of the previous block into the other buffer.  The block's 32 KB
     // are 32 pieces of 1 KB; wave w fills pieces P w .. P w + P - 1 (P =
     // 32 / W; rows 8q .. 8q+7 of piece q, lane l in slot l: row 8q + l/8,
-    // physical chunk l%8 holding logical chunk (l%8) ^ ((row >> 1) & 7)), and
+    // physical chunk l%8 holding logical chunk (l%8) ^ lds_swz_fp8(row)), and
     // in the row-scaled mode waves 0..3 load the scales of rows 64w + lane.
     // The compiler waits for those loads before the block's first LDS read
     // (it cannot tell the two buffers apart), so their latency is only
@@ -117,7 +116,7 @@ __global__ __launch_bounds__(MODE == kScaleRow ? 512 : 256, MODE == kScaleRow ? 
 #pragma unroll
     for (int t = 0; t < kPieces; ++t) {
         const int row = 8 * (kPieces * wave + t) + (lane >> 3);
-        const int c = (lane & 7) ^ ((row >> 1) & 7);
+        const int c = (lane & 7) ^ lds_swz_fp8(row);
         bd_src[t] = B + min(j0 + row, J - 1) * Kc + 16 * c;
     }
     const float* sbd_src =
@@ -249,8 +248,9 @@ __global__ __launch_bounds__(MODE == kScaleRow ? 512 : 256, MODE == kScaleRow ? 
         }
         auto frag = [&](int js) __attribute__((always_inline)) {
             const int row = 16 * js + r16;
-            const uint4 lo = *reinterpret_cast<const uint4*>(Bt + lds_off(row, 2 * g));
-            const uint4 hi = *reinterpret_cast<const uint4*>(Bt + lds_off(row, 2 * g + 1));
+            const int swz = lds_swz_fp8(row);
+            const uint4 lo = *reinterpret_cast<const uint4*>(Bt + lds_off(row, 2 * g, swz));
+            const uint4 hi = *reinterpret_cast<const uint4*>(Bt + lds_off(row, 2 * g + 1, swz));
             return as_v8i(lo, hi);
         };
         // Row-scaled mode: the scale products of one group's outputs, formed
