@@ -46,14 +46,21 @@ def _check_dims(t: int, d_in: int, d_out: int) -> None:
 def _weight_grad(weight, workspace, mfma8: bool, dytq, dyts, xtq, xts):
     """dW = dY^T X of one linear layer from the token-axis codes of dY and X:
     returned in FP32, or, when the weight carries an FP32 ``main_grad``, added
-    into it (by the wgrad GEMM itself on the exact path) and None returned."""
+    into it (by the wgrad GEMM itself on the exact path) and None returned.
+    A workspace smaller than the call's query for this shape (or none) is
+    replaced by one allocated for the call."""
     main = getattr(weight, "main_grad", None)
-    ws_arg = workspace if workspace is not None else "auto"
     M, N, K = xtq.shape[1], dytq.shape[0], xtq.shape[0]
     if mfma8:
-        need = B.fp8_gemm_wgrad_mfma8_workspace_bytes(M, N, K)
-        if workspace is not None and workspace.numel() < need:
-            ws_arg = "auto"
+        query = B.fp8_gemm_wgrad_mfma8_workspace_bytes
+    elif main is not None:
+        query = B.fp8_gemm_wgrad_accumulate_workspace_bytes
+    else:
+        query = B.fp8_gemm_wgrad_workspace_bytes
+    ws_arg = workspace
+    if workspace is None or workspace.numel() < query(M, N, K):
+        ws_arg = "auto"
+    if mfma8:
         dw32 = B.fp8_gemm_wgrad_mfma8(dytq, dyts, xtq, xts, workspace=ws_arg)
         if main is None:
             return dw32
@@ -61,9 +68,6 @@ def _weight_grad(weight, workspace, mfma8: bool, dytq, dyts, xtq, xts):
         return None
     if main is not None:
         # Summed into main_grad by the GEMM itself (no separate pass).
-        need = B.fp8_gemm_wgrad_accumulate_workspace_bytes(M, N, K)
-        if workspace is not None and workspace.numel() < need:
-            ws_arg = "auto"
         B.fp8_gemm_wgrad_accumulate(dytq, dyts, xtq, xts, main, workspace=ws_arg)
         return None
     return B.fp8_gemm_wgrad(dytq, dyts, xtq, xts, workspace=ws_arg)

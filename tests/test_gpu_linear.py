@@ -130,3 +130,30 @@ def test_fp8_linear_mfma8_runs_the_mfma8_gemms():
     ry, rdx, rdw, deq = _oracle_layer(xb, wb, dyb)
     check_mfma8(to_np(lin.weight.main_grad), rdw, deq["dyt"], deq["xt"], "Fp8Linear(mfma8) dW")
     check_mfma8(to_np(y), ry, deq["x"], deq["w"], "Fp8Linear(mfma8) Y", bf16=True)
+
+
+def test_fp8_linear_small_workspace_is_replaced():
+    """A workspace smaller than the wgrad's query (16 bytes, where the
+    4096-token contraction of a 384 x 256 weight is split) is replaced by one
+    allocated for the call, on the exact path with and without main_grad:
+    the gradients equal those of a layer given no workspace, bit for bit."""
+    T, d_in, d_out = 4096, 256, 384
+    assert fp8.fp8_gemm_wgrad_workspace_bytes(T, d_out, d_in) > 16
+    xb = inputs.normal((46, T, d_in), (T, d_in), 1.0)
+    wb = inputs.normal((47, d_out, d_in), (d_out, d_in), 0.02)
+    dyb = inputs.student_t((48, T, d_out), (T, d_out), 3.0, 1e-3)
+    for with_main in (False, True):
+        grads = []
+        for ws in (None, torch.empty(16, dtype=torch.uint8, device="cuda")):
+            lin = fp8.Fp8Linear(d_in, d_out, device="cuda", workspace=ws)
+            with torch.no_grad():
+                lin.weight.copy_(to_dev_bf16(wb))
+            if with_main:
+                lin.weight.main_grad = torch.zeros(d_out, d_in, dtype=torch.float32, device="cuda")
+            x = to_dev_bf16(xb).requires_grad_(True)
+            lin(x).backward(to_dev_bf16(dyb))
+            torch.cuda.synchronize()
+            dw = lin.weight.main_grad if with_main else lin.weight.grad
+            grads.append((dw.clone(), x.grad.clone()))
+        _say(f"Fp8Linear small workspace main_grad={with_main}")
+        assert torch.equal(grads[0][0], grads[1][0]) and torch.equal(grads[0][1], grads[1][1])
