@@ -247,14 +247,47 @@ struct DualPlain {
     }
 };
 
+// Gates below kLowGate.  There 1 + e^g is 1 in FP32, so sigmoid(g) equals
+// e^g and 1 - sigmoid(g) equals 1 to FP32 precision.  Further down, e^-g
+// overflows FP32 (g < -88.7) and 1 / (1 + e^-g) is an FP32 denormal
+// (g < -87.3), while the products that contain sigmoid(g) can still be normal
+// BF16 values (BF16 reaches down to 2^-133, and |u| up to 2^128).  So below
+// kLowGate those products are formed from logarithms (exp_product).
+constexpr float kLowGate = -64.0f;
+
+// log2|x| for finite x != 0, FP32 denormals included (scaled by 2^64 first).
+__device__ __forceinline__ float log2_abs(float x) {
+    const float a = fabsf(x);
+    return a < 1.17549435e-38f ? __log2f(a * 18446744073709551616.0f) - 64.0f : __log2f(a);
+}
+
+// x y z e^g for g < kLowGate, with any finite x, y, z:
+// sign(x y z) 2^L, L = log2|x| + log2|y| + log2|z| + g log2(e).  The integer
+// part of L is applied by ldexp (a single rounding, into the denormals when
+// the result is that small), the fraction by the hardware exponential.  L's
+// rounding (an absolute error near 2^-15 at g = -300) makes the relative
+// error near 2^-15, far inside BF16's 2^-9 rounding step.
+__device__ __forceinline__ float exp_product(float g, float x, float y, float z) {
+    const uint32_t sign =
+        (__float_as_uint(x) ^ __float_as_uint(y) ^ __float_as_uint(z)) & 0x80000000u;
+    if (x == 0.0f || y == 0.0f || z == 0.0f) return __uint_as_float(sign);
+    // Below 2^-300 the result is zero in FP32; the floor keeps the exponent an int.
+    const float l =
+        fmaxf(log2_abs(x) + log2_abs(y) + log2_abs(z) + g * 1.44269504f, -300.0f);
+    const float n = floorf(l);
+    const float r = ldexpf(__builtin_amdgcn_exp2f(l - n), (int)n);
+    return __uint_as_float(__float_as_uint(r) | sign);
+}
+
 // SwiGLU of the MLP, formed on the way in: h = silu(g) * u, silu(g) =
 // g / (1 + e^-g), in FP32 and rounded to BF16 (ties to even), with the gate g
 // in columns 0..F-1 of the gate/up projection's output [M, 2F] and the up
 // value u in columns F..2F-1.  The exponential and the reciprocal are the
 // hardware approximations (relative error near 2^-20 for the gates of real
-// activations), far inside BF16's 2^-9 rounding step.  H itself is stored
-// only when h is given.
+// activations), far inside BF16's 2^-9 rounding step; below kLowGate,
+// h = g u e^g by exp_product.  H itself is stored only when h is given.
 __device__ __forceinline__ float swiglu_f32(float g, float u) {
+    if (g < kLowGate) return exp_product(g, g, u, 1.0f);
     return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 struct DualSwiglu {
@@ -279,17 +312,23 @@ struct DualSwiglu {
 // s (1 + g (1 - s)) with s = 1 / (1 + e^-g), and the up half (column F + f)
 // is d_up = dh * silu(g) = dh * g * s, each rounded to BF16.  1 - s is taken
 // as e^-g * s for g >= 0 (no cancellation as s nears 1) and as 1 - s below
-// (where s < 1/2).  One workgroup quantizes the gate tile and then the up
-// tile of the same tokens and columns f: the first pass keeps the thread's dh
-// and g in registers for the second, so each input is read once.  The BF16
-// gradient is stored only when dgu is given.
+// (where s < 1/2).  Below kLowGate, s = e^g and 1 - s = 1, so d_gate =
+// dh u (1 + g) e^g and d_up = dh g e^g, both by exp_product.  Above it the
+// products are formed in FP32 in the order written, which is exact to FP32
+// rounding as long as dh * u stays inside the FP32 range.  One workgroup
+// quantizes the gate tile and then the up tile of the same tokens and
+// columns f: the first pass keeps the thread's dh and g in registers for the
+// second, so each input is read once.  The BF16 gradient is stored only when
+// dgu is given.
 __device__ __forceinline__ float swiglu_bwd_gate_f32(float d, float g, float u) {
+    if (g < kLowGate) return exp_product(g, d, u, 1.0f + g);
     const float e = __expf(-g);
     const float sg = __builtin_amdgcn_rcpf(1.0f + e);
     const float om = g >= 0.0f ? e * sg : 1.0f - sg;
     return d * u * (sg * (1.0f + g * om));
 }
 __device__ __forceinline__ float swiglu_bwd_up_f32(float d, float g) {
+    if (g < kLowGate) return exp_product(g, d, g, 1.0f);
     return d * (g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)));
 }
 struct SwigluBwdRegs {
