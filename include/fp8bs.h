@@ -174,9 +174,11 @@ fp8bs_status fp8_quantize_dual(const uint16_t* x, int64_t M, int64_t C, uint8_t*
  *   h   bf16 [M, F] or NULL                  H itself, when given
  * silu(g) = g / (1 + e^-g), evaluated with the hardware exponential and
  * reciprocal (relative error about 2^-20 at the gate values of real
- * activations), so H is within one BF16 unit of the exactly rounded value and
- * the codes are those of fp8_quantize_dual applied to the H this call forms.
- * M, F >= 0 and multiples of 128.  Inputs must be finite.
+ * activations; below g = -64, where e^-g overflows or the sigmoid is an FP32
+ * denormal, H = g u e^g is formed from logarithms, relative error near
+ * 2^-15), so H is within one BF16 unit of the exactly rounded value for any
+ * finite inputs and the codes are those of fp8_quantize_dual applied to the
+ * H this call forms.  M, F >= 0 and multiples of 128.  Inputs must be finite.
  */
 fp8bs_status fp8_swiglu_quantize_dual(const uint16_t* gate_up, int64_t M, int64_t F, uint8_t* q,
                                       float* s, uint8_t* qt, float* st, uint16_t* h,
@@ -196,6 +198,9 @@ fp8bs_status fp8_swiglu_quantize_dual(const uint16_t* gate_up, int64_t M, int64_
  * r[m] = 1 / sqrt(mean_c x[m][c]^2 + eps) (squares summed in FP32, correctly
  * rounded square root and division); Y = x * r * gamma in FP32, rounded to
  * BF16; the codes are those of fp8_quantize_dual applied to that BF16 Y.
+ * Rows whose sum of squares leaves the FP32 range (|x| above about 1e19, or,
+ * with eps below about 1e-30, all |x| below about 1e-19) are outside the
+ * call's range: their r and Y are unspecified.
  * Two launches on stream (r, then the quantized tiles).  M, C >= 0 and
  * multiples of 128 (nothing is written when either is 0); FP8BS_ERR_VALUE
  * for a negative or non-finite eps.
@@ -217,9 +222,12 @@ fp8bs_status fp8_rmsnorm_quantize_dual(const uint16_t* x, const uint16_t* gamma,
  *   dgate_up bf16 [M, 2F] or NULL            dGU itself, when given
  * dGU[:, f] = dh * u * silu'(g) (gate half), dGU[:, F + f] = dh * silu(g)
  * (up half), silu'(g) = s (1 + g (1 - s)), s = 1 / (1 + e^-g), each formed in
- * FP32 with the hardware exponential and reciprocal and rounded to BF16; the
- * codes are those of fp8_quantize_dual applied to that BF16 dGU.
- * M, F >= 0 and multiples of 128.  Inputs must be finite.
+ * FP32 with the hardware exponential and reciprocal and rounded to BF16
+ * (below g = -64, dh u (1 + g) e^g and dh g e^g from logarithms, as in
+ * fp8_swiglu_quantize_dual); the codes are those of fp8_quantize_dual
+ * applied to that BF16 dGU.  Above g = -64 the FP32 products need dh * u
+ * inside the FP32 range.  M, F >= 0 and multiples of 128.  Inputs must be
+ * finite.
  */
 fp8bs_status fp8_swiglu_backward_quantize_dual(const uint16_t* dh, const uint16_t* gate_up,
                                                int64_t M, int64_t F, uint8_t* q, float* s,
