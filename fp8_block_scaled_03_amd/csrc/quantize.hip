@@ -562,8 +562,46 @@ __global__ __launch_bounds__(256) void rmsnorm_rstd_kernel(const uint16_t* __res
             }
         }
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) ss += __shfl_xor(ss, o);
-        if (lane == 0) rstd[row] = 1.0f / sqrtf(ss / (float)C + eps);
+        for (int o = 1; o < 64; o <<= 1) ss += __shfl_xor(ss, o);   // the same sum in every lane
+        float r = 1.0f / sqrtf(ss / (float)C + eps);
+        // The sum of squares left FP32's range: it overflowed (|x| above
+        // about 1e19), or the squares underflowed (every |x| below about
+        // 2^-50) while eps is too small to dominate them.  Such a row is
+        // summed again as x 2^-k, k the exponent of its largest |x|, and
+        // r = 2^-k / sqrt(mean((x 2^-k)^2) + eps 2^-2k).
+        if (!(ss <= 3.0e38f) || (ss < 0x1p-100f && eps < 0x1p-60f)) {
+            float amax = 0.f;
+            for (int64_t c = 8 * lane; c < C; c += 512) {
+                const uint4 v = load_stream16(xr + c);
+                amax = fmaxf(amax, __uint_as_float(absmax_fold(absmax_u4(0u, v)) << 16));
+            }
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+            if (amax > 0.f) {
+                int k;
+                frexpf(amax, &k);                       // amax = m 2^k, m in [1/2, 1)
+                float s2 = 0.f;
+                for (int64_t c = 8 * lane; c < C; c += 512) {
+                    const uint4 v = load_stream16(xr + c);
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float a = ldexpf(bf16_lo(w[j]), -k), b = ldexpf(bf16_hi(w[j]), -k);
+                        s2 = __builtin_fmaf(a, a, s2);
+                        s2 = __builtin_fmaf(b, b, s2);
+                    }
+                }
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) s2 += __shfl_xor(s2, o);
+                int ke = 0;
+                if (eps > 0.f) frexpf(eps, &ke);
+                // eps 2^-2k above 2^100 dominates the mean (at most 1) beyond FP32 precision
+                r = (eps > 0.f && ke - 2 * k > 100)
+                        ? 1.0f / sqrtf(eps)
+                        : ldexpf(1.0f / sqrtf(s2 / (float)C + ldexpf(eps, -2 * k)), -k);
+            }
+        }
+        if (lane == 0) rstd[row] = r;
     }
 }
 

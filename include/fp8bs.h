@@ -198,9 +198,10 @@ fp8bs_status fp8_swiglu_quantize_dual(const uint16_t* gate_up, int64_t M, int64_
  * r[m] = 1 / sqrt(mean_c x[m][c]^2 + eps) (squares summed in FP32, correctly
  * rounded square root and division); Y = x * r * gamma in FP32, rounded to
  * BF16; the codes are those of fp8_quantize_dual applied to that BF16 Y.
- * Rows whose sum of squares leaves the FP32 range (|x| above about 1e19, or,
- * with eps below about 1e-30, all |x| below about 1e-19) are outside the
- * call's range: their r and Y are unspecified.
+ * A row whose sum of squares leaves FP32's range (|x| above about 1e19, or
+ * every |x| below about 2^-50 with eps below 2^-60) is summed again scaled by
+ * a power of two, so any finite row is in range except those whose r itself
+ * exceeds FP32 (every |x| a BF16 subnormal, eps below about 1e-77).
  * Two launches on stream (r, then the quantized tiles).  M, C >= 0 and
  * multiples of 128 (nothing is written when either is 0); FP8BS_ERR_VALUE
  * for a negative or non-finite eps.

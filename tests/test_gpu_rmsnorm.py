@@ -143,3 +143,19 @@ def test_rmsnorm_dual_rows_past_one_grid_pass():
         assert np.array_equal(to_np(st[:, mb:mb + 1]).view(np.uint32), ost.view(np.uint32))
     del x, q, s, qt, st, r, y
     torch.cuda.empty_cache()
+
+
+def test_rmsnorm_dual_rows_outside_fp32_squares():
+    """Rows whose sum of squares leaves FP32's range are summed again at a
+    power-of-two scale: rows of N(0,1) x 1e25 (the squares overflow), x 1e36,
+    x 1e-25 and x 1e-35 (the squares underflow) with eps = 0, the tiny rows
+    also with eps = 1e-6 (which then dominates), beside ordinary rows."""
+    M, C = 256, 384
+    base = inputs.normal((138, M, C), (M, C), 1.0)
+    vals = oracle.bf16_to_f32(base).astype(np.float64)
+    scale = np.ones(M)
+    scale[0:32], scale[32:64], scale[64:96], scale[96:128] = 1e25, 1e36, 1e-25, 1e-35
+    x = inputs.bf16_bits((vals * scale[:, None]).astype(np.float32))
+    g = _gamma(C, 139)
+    _check(x, g, 0.0, "rmsnorm extreme rows eps=0")
+    _check(np.ascontiguousarray(x[64:192]), g, 1e-6, "rmsnorm tiny rows eps=1e-6")
