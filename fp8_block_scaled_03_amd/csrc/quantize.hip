@@ -314,8 +314,9 @@ struct DualSwiglu {
 // as e^-g * s for g >= 0 (no cancellation as s nears 1) and as 1 - s below
 // (where s < 1/2).  Below kLowGate, s = e^g and 1 - s = 1, so d_gate =
 // dh u (1 + g) e^g and d_up = dh g e^g, both by exp_product.  Above it the
-// products are formed in FP32 in the order written, which is exact to FP32
-// rounding as long as dh * u stays inside the FP32 range.  One workgroup
+// products are formed in FP32 in the order written, each rounding once; where
+// dh * u overflows FP32 (the gradient itself need not, silu'(g) being as
+// small as 1e-26 there), d_gate comes from logarithms too.  One workgroup
 // quantizes the gate tile and then the up tile of the same tokens and
 // columns f: the first pass keeps the thread's dh and g in registers for the
 // second, so each input is read once.  The BF16 gradient is stored only when
@@ -325,7 +326,10 @@ __device__ __forceinline__ float swiglu_bwd_gate_f32(float d, float g, float u) 
     const float e = __expf(-g);
     const float sg = __builtin_amdgcn_rcpf(1.0f + e);
     const float om = g >= 0.0f ? e * sg : 1.0f - sg;
-    return d * u * (sg * (1.0f + g * om));
+    const float ds = sg * (1.0f + g * om);
+    const float du = d * u;
+    if (!(fabsf(du) <= 3.40282347e38f)) return exp_product(0.0f, d, u, ds);
+    return du * ds;
 }
 __device__ __forceinline__ float swiglu_bwd_up_f32(float d, float g) {
     if (g < kLowGate) return exp_product(g, d, g, 1.0f);

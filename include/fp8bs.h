@@ -226,9 +226,9 @@ fp8bs_status fp8_rmsnorm_quantize_dual(const uint16_t* x, const uint16_t* gamma,
  * FP32 with the hardware exponential and reciprocal and rounded to BF16
  * (below g = -64, dh u (1 + g) e^g and dh g e^g from logarithms, as in
  * fp8_swiglu_quantize_dual); the codes are those of fp8_quantize_dual
- * applied to that BF16 dGU.  Above g = -64 the FP32 products need dh * u
- * inside the FP32 range.  M, F >= 0 and multiples of 128.  Inputs must be
- * finite.
+ * applied to that BF16 dGU (where dh * u overflows FP32 the gate half is also
+ * formed from logarithms, so any finite inputs whose gradient is finite are
+ * in range).  M, F >= 0 and multiples of 128.  Inputs must be finite.
  */
 fp8bs_status fp8_swiglu_backward_quantize_dual(const uint16_t* dh, const uint16_t* gate_up,
                                                int64_t M, int64_t F, uint8_t* q, float* s,

@@ -184,3 +184,19 @@ def test_swiglu_backward_dual_very_negative_gates():
     mag = 10.0 ** rng.uniform(-20, 20, (M, F))
     dh = inputs.bf16_bits(np.where(rng.random((M, F)) < 0.5, -mag, mag).astype(np.float32))
     _check_bwd(dh, gu, "swiglu backward low gates", equal_frac=0.95)
+
+
+def test_swiglu_backward_dual_overflowing_dh_times_up():
+    """Gates from -64 to -40, where silu'(g) is 1e-26 to 1e-16, with dH and
+    up values from 1e15 to 1e25: dH * u overflows FP32 on many elements while
+    the gate gradient dH * u * silu'(g) stays finite (below 1e35)."""
+    M, F = 256, 256
+    rng = np.random.default_rng(130)
+    gate = rng.uniform(-64.0, -40.0, (M, F))
+    mag = lambda: 10.0 ** rng.uniform(15, 25, (M, F)) * np.where(rng.random((M, F)) < 0.5, -1, 1)
+    as_bits = lambda v: inputs.bf16_bits(np.asarray(v, dtype=np.float32))
+    gu = np.ascontiguousarray(np.concatenate([as_bits(gate), as_bits(mag())], axis=1))
+    dh = as_bits(mag())
+    prod = oracle.bf16_to_f32(dh).astype(np.float64) * oracle.bf16_to_f32(gu[:, F:]).astype(np.float64)
+    assert (np.abs(prod) > 3.4e38).mean() > 0.2
+    _check_bwd(dh, gu, "swiglu backward dh*u overflow", equal_frac=0.95)
