@@ -83,13 +83,16 @@ __global__ __launch_bounds__(kB16Threads, 1) void gemm_bf16_kernel(
         const int buf = ks & 1;
         wait_global_loads();
         __syncthreads();
-        if (ks + 1 < nks) issue_loads(ks + 1, buf ^ 1);
 
         const uint8_t* At = As[buf];
         const uint8_t* Bt = Bs[buf];
         // MFMA chunk c covers K = 32c .. 32c+31 of the step; lane (r16, g)
         // supplies K = 32c + 8g .. +7 of its row: 16-byte chunk 4c + g.
-        v8bf af[4][2];
+        // Every fragment of the step is read before the next step's direct
+        // loads are issued: the compiler waits for all outstanding direct
+        // loads before an LDS read (it cannot tell the two buffers apart),
+        // so reads issued after them would wait for the next step's data.
+        v8bf af[4][2], bfr[8][2];
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int row = wi * 64 + it * 16 + r16;
@@ -101,10 +104,15 @@ __global__ __launch_bounds__(kB16Threads, 1) void gemm_bf16_kernel(
 #pragma unroll
         for (int js = 0; js < 8; ++js) {
             const int row = wj * 128 + js * 16 + r16;
-            v8bf bf[2];
 #pragma unroll
             for (int c = 0; c < 2; ++c)
-                bf[c] = *reinterpret_cast<const v8bf*>(Bt + lds_off(row, 4 * c + g, lds_swz_bf16(row)));
+                bfr[js][c] =
+                    *reinterpret_cast<const v8bf*>(Bt + lds_off(row, 4 * c + g, lds_swz_bf16(row)));
+        }
+        if (ks + 1 < nks) issue_loads(ks + 1, buf ^ 1);
+#pragma unroll
+        for (int js = 0; js < 8; ++js) {
+            const v8bf* bf = bfr[js];
 #pragma unroll
             for (int c = 0; c < 2; ++c)
 #pragma unroll
