@@ -440,7 +440,7 @@ fp8bs_status bf16_gemm_tn(const uint16_t* a, const uint16_t* b, void* c, fp8bs_o
     if (out_empty) return FP8BS_OK;
     int cus;
     FP8BS_TRY(check_device(&cus));
-    return launched(fp8bs::launch_gemm_bf16(a, b, c, cv == FP8BS_OUT_BF16, I, J, K, stream));
+    return launched(fp8bs::launch_gemm_bf16(a, b, c, cv == FP8BS_OUT_BF16, I, J, K, cus, stream));
 }
 
 fp8bs_status fp8_encode_e4m3(const float* x, int64_t n, uint8_t* q, fp8bs_stream_t stream) {

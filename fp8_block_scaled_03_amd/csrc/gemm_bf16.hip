@@ -11,8 +11,10 @@
 // a 64x128 patch of 4x8 MFMA tiles; BF16 tiles (256 rows of 128 bytes, 32 KB
 // per operand) double-buffered in LDS through direct global->LDS loads;
 // v_mfma_f32_16x16x32_bf16 accumulates straight into the FP32 accumulators
-// (nothing to widen, no per-block scale fold).  This wave's A fragments for
-// the 64-wide step are read once and kept in registers; B fragments stream.
+// (nothing to widen, no per-block scale fold).  A step's A and B fragments
+// are read into registers before the next step's loads are issued.  Grids
+// whose 256 x 256 tiles would leave half the CUs idle (weight-gradient
+// shapes, whose outputs are small) run 128 x 128 tiles of four waves.
 #include "device_common.h"
 #include "gemm_common.h"
 #include "internal.h"
@@ -21,40 +23,43 @@ namespace fp8bs {
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-constexpr int kB16M = 256;
-constexpr int kB16N = 256;
 constexpr int kB16K = 64;                       // BF16 values per 128-byte tile row
-constexpr int kB16Threads = 512;
-constexpr int kB16Tile = kB16M * kRowBytes;     // one operand tile: 32 KB
 
-template <bool OUT_BF16>
-__global__ __launch_bounds__(kB16Threads, 1) void gemm_bf16_kernel(
+// T x T output tiles (T = 256 or 128) of 2 T / 64 waves in a (T/64) x 2 grid,
+// each wave a 64 x T/2 patch of 4 x T/32 MFMA tiles.  T = 128 (four waves,
+// two workgroups per CU) serves grids that the 256 x 256 tiles leave
+// partly idle.
+template <int T, bool OUT_BF16>
+__global__ __launch_bounds__(2 * T, T == 256 ? 1 : 2) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, void* __restrict__ C,
     int64_t I, int64_t J, int64_t K, int tiles_i, int tiles_j) {
-    __shared__ __align__(16) uint8_t As[2][kB16Tile];
-    __shared__ __align__(16) uint8_t Bs[2][kB16Tile];
+    constexpr int WI = T / 64;                  // waves along i; also the loading waves
+    constexpr int JS = T / 32;                  // B subtiles per wave
+    constexpr int kTile = T * kRowBytes;        // one operand tile
+    __shared__ __align__(16) uint8_t As[2][kTile];
+    __shared__ __align__(16) uint8_t Bs[2][kTile];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wi = wave & 3, wj = wave >> 2;
+    const int wi = wave % WI, wj = wave / WI;
     int ti, tj;
     tile_coords(blockIdx.x, tiles_i, tiles_j, &ti, &tj);
-    const int64_t i0 = (int64_t)ti * kB16M, j0 = (int64_t)tj * kB16N;
+    const int64_t i0 = (int64_t)ti * T, j0 = (int64_t)tj * T;
     const int nks = (int)(K / kB16K);
     const int64_t row_bytes = K * 2;
 
-    // Direct global -> LDS loads.  Waves 0..3 fill both 32 KB tiles (wave w:
+    // Direct global -> LDS loads.  Waves 0 .. WI-1 fill both tiles (wave w:
     // 1 KB pieces 8w .. 8w+7, 8 rows each; lane l lands at row 8*piece + l/8,
     // physical chunk l%8, and fetches the logical chunk the swizzle puts
-    // there); waves 4..7 go straight on to their MFMAs after each barrier.
+    // there); the other waves go straight on to their MFMAs after each barrier.
     // Rows past the end of A or B are clamped to the last row (never stored).
     const uint8_t* a_bytes = reinterpret_cast<const uint8_t*>(A);
     const uint8_t* b_bytes = reinterpret_cast<const uint8_t*>(B);
-    const int prow = 64 * (wave & 3) + (lane >> 3);
+    const int prow = 64 * wave + (lane >> 3);
     const int pc = (lane & 7) ^ lds_swz_bf16(prow);
     auto issue_loads = [&](int ks, int buf) {
-        if (wave >= 4) return;
+        if (wave >= WI) return;
         const int64_t koff = (int64_t)ks * kRowBytes;
         int pr = prow, pcc = pc;
         asm volatile("" : "+v"(pr), "+v"(pcc));       // keep the address math per call
@@ -69,11 +74,11 @@ __global__ __launch_bounds__(kB16Threads, 1) void gemm_bf16_kernel(
         }
     };
 
-    v4f acc[4][8];
+    v4f acc[4][JS];
 #pragma unroll
     for (int it = 0; it < 4; ++it)
 #pragma unroll
-        for (int js = 0; js < 8; ++js) acc[it][js] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int js = 0; js < JS; ++js) acc[it][js] = v4f{0.f, 0.f, 0.f, 0.f};
 
     const int r16 = lane & 15;
     const int g = lane >> 4;
@@ -92,7 +97,7 @@ __global__ __launch_bounds__(kB16Threads, 1) void gemm_bf16_kernel(
         // loads are issued: the compiler waits for all outstanding direct
         // loads before an LDS read (it cannot tell the two buffers apart),
         // so reads issued after them would wait for the next step's data.
-        v8bf af[4][2], bfr[8][2];
+        v8bf af[4][2], bfr[JS][2];
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int row = wi * 64 + it * 16 + r16;
@@ -102,8 +107,8 @@ __global__ __launch_bounds__(kB16Threads, 1) void gemm_bf16_kernel(
                     *reinterpret_cast<const v8bf*>(At + lds_off(row, 4 * c + g, lds_swz_bf16(row)));
         }
 #pragma unroll
-        for (int js = 0; js < 8; ++js) {
-            const int row = wj * 128 + js * 16 + r16;
+        for (int js = 0; js < JS; ++js) {
+            const int row = wj * (T / 2) + js * 16 + r16;
 #pragma unroll
             for (int c = 0; c < 2; ++c)
                 bfr[js][c] =
@@ -111,7 +116,7 @@ __global__ __launch_bounds__(kB16Threads, 1) void gemm_bf16_kernel(
         }
         if (ks + 1 < nks) issue_loads(ks + 1, buf ^ 1);
 #pragma unroll
-        for (int js = 0; js < 8; ++js) {
+        for (int js = 0; js < JS; ++js) {
             const v8bf* bf = bfr[js];
 #pragma unroll
             for (int c = 0; c < 2; ++c)
@@ -125,19 +130,20 @@ __global__ __launch_bounds__(kB16Threads, 1) void gemm_bf16_kernel(
 
     // epilogue: lane owns C[i][j .. j+3]
     if constexpr (OUT_BF16) __syncthreads();         // every wave done with the LDS tiles
-    if (j0 + 128 * wj >= J) return;
+    if (j0 + (T / 2) * wj >= J) return;
     if constexpr (OUT_BF16) {
-        // Restage the wave's 64x128 BF16 patch through LDS so that it leaves
-        // as whole 256-byte rows in 16-byte stores (chunks XOR-swizzled by row).
-        uint8_t* stage = (wave < 4 ? &As[0][0] : &Bs[0][0]) + (wave & 3) * 16384;
+        // Restage the wave's 64 x T/2 BF16 patch through LDS so that it leaves
+        // as whole T-byte rows in 16-byte stores (chunks XOR-swizzled by row).
+        constexpr int CH = T / 16;                       // 16-byte chunks per staged row
+        uint8_t* stage = (wave < 4 ? &As[0][0] : &Bs[0][0]) + (wave & 3) * (64 * T);
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int row = it * 16 + r16;
 #pragma unroll
-            for (int js = 0; js < 8; ++js) {
+            for (int js = 0; js < JS; ++js) {
                 const int b = js * 32 + g * 8;
-                const int phys = (((b >> 4) ^ (row & 15)) << 4) | (b & 15);
-                *reinterpret_cast<uint2*>(stage + row * 256 + phys) =
+                const int phys = (((b >> 4) ^ (row & (CH - 1))) << 4) | (b & 15);
+                *reinterpret_cast<uint2*>(stage + row * T + phys) =
                     make_uint2(pack_bf16x2(acc[it][js][0], acc[it][js][1]),
                                pack_bf16x2(acc[it][js][2], acc[it][js][3]));
             }
@@ -146,13 +152,13 @@ __global__ __launch_bounds__(kB16Threads, 1) void gemm_bf16_kernel(
         __builtin_amdgcn_wave_barrier();
         uint16_t* Cb = reinterpret_cast<uint16_t*>(C);
 #pragma unroll
-        for (int pass = 0; pass < 16; ++pass) {
-            const int row = pass * 4 + (lane >> 4);
-            const int c = lane & 15;
+        for (int pass = 0; pass < CH; ++pass) {
+            const int row = pass * (64 / CH) + lane / CH;
+            const int c = lane % CH;
             const uint4 w =
-                *reinterpret_cast<const uint4*>(stage + row * 256 + ((c ^ (row & 15)) << 4));
+                *reinterpret_cast<const uint4*>(stage + row * T + ((c ^ (row & (CH - 1))) << 4));
             const int64_t i = i0 + wi * 64 + row;
-            if (i < I) *reinterpret_cast<uint4*>(Cb + i * J + j0 + wj * 128 + c * 8) = w;
+            if (i < I) *reinterpret_cast<uint4*>(Cb + i * J + j0 + wj * (T / 2) + c * 8) = w;
         }
         return;
     }
@@ -161,8 +167,8 @@ __global__ __launch_bounds__(kB16Threads, 1) void gemm_bf16_kernel(
         const int64_t i = i0 + wi * 64 + it * 16 + r16;
         if (i >= I) continue;
 #pragma unroll
-        for (int js = 0; js < 8; ++js) {
-            const int64_t j = j0 + wj * 128 + js * 16 + 4 * g;
+        for (int js = 0; js < JS; ++js) {
+            const int64_t j = j0 + wj * (T / 2) + js * 16 + 4 * g;
             if (OUT_BF16) {
                 uint2 pk;
                 pk.x = pack_bf16x2(acc[it][js][0], acc[it][js][1]);
@@ -176,17 +182,31 @@ __global__ __launch_bounds__(kB16Threads, 1) void gemm_bf16_kernel(
     }
 }
 
-hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* B, void* C, bool out_bf16,
-                            int64_t I, int64_t J, int64_t K, hipStream_t stream) {
-    const int64_t tiles_i = (I + kB16M - 1) / kB16M;
-    const int64_t tiles_j = (J + kB16N - 1) / kB16N;
+template <int T>
+static hipError_t launch_bf16_tiles(const uint16_t* A, const uint16_t* B, void* C, bool out_bf16,
+                                    int64_t I, int64_t J, int64_t K, hipStream_t stream) {
+    const int64_t tiles_i = (I + T - 1) / T;
+    const int64_t tiles_j = (J + T - 1) / T;
     const int64_t blocks = tiles_i * tiles_j;
     if (blocks == 0) return hipSuccess;
     if (out_bf16)
-        return launch(gemm_bf16_kernel<true>, grid1d(blocks), dim3(kB16Threads), stream, A,
-                      B, C, I, J, K, (int)tiles_i, (int)tiles_j);
-    return launch(gemm_bf16_kernel<false>, grid1d(blocks), dim3(kB16Threads), stream, A, B,
-                  C, I, J, K, (int)tiles_i, (int)tiles_j);
+        return launch(gemm_bf16_kernel<T, true>, grid1d(blocks), dim3(2 * T), stream, A, B, C, I,
+                      J, K, (int)tiles_i, (int)tiles_j);
+    return launch(gemm_bf16_kernel<T, false>, grid1d(blocks), dim3(2 * T), stream, A, B, C, I, J,
+                  K, (int)tiles_i, (int)tiles_j);
+}
+
+// The 256 x 256 tile once it gives more than half the CUs a tile; below that
+// the 128 x 128 tile (four times the workgroups, two per CU), which is the
+// slower of the two per CU: at 2048 x 2048 outputs (64 large tiles) it took
+// 27% less time, at 4096 x 2048 (128) 10% less, and at 2048 x 6144 (192) 55%
+// more, with a 16,384-long contraction.
+hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* B, void* C, bool out_bf16,
+                            int64_t I, int64_t J, int64_t K, int num_cus, hipStream_t stream) {
+    const int64_t big_tiles = ((I + 255) / 256) * ((J + 255) / 256);
+    if (2 * big_tiles > (num_cus > 0 ? num_cus : 256))
+        return launch_bf16_tiles<256>(A, B, C, out_bf16, I, J, K, stream);
+    return launch_bf16_tiles<128>(A, B, C, out_bf16, I, J, K, stream);
 }
 
 }  // namespace fp8bs

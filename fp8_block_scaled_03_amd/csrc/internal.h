@@ -147,7 +147,7 @@ hipError_t launch_wgrad_noalloc(const uint8_t* dytq, const float* dyts, const ui
 
 // C[I, J] = A B^T with A [I, K], B [J, K] BF16 (unquantized comparator).
 hipError_t launch_gemm_bf16(const uint16_t* A, const uint16_t* B, void* C, bool out_bf16,
-                            int64_t I, int64_t J, int64_t K, hipStream_t stream);
+                            int64_t I, int64_t J, int64_t K, int num_cus, hipStream_t stream);
 
 // Diagnostic: y0[i] = high byte of x[i], y1[i] (if y1) = low byte (hbm_rate_kernel).
 hipError_t launch_hbm_rate(const uint16_t* x, int64_t n, uint8_t* y0, uint8_t* y1,

@@ -64,7 +64,7 @@ def test_bf16_gemm_empty_and_zero_k():
     assert torch.count_nonzero(c).item() == 0
 
 
-@pytest.mark.parametrize("I,J,K", [(16384, 4096, 2048), (16384, 2048, 6144)])
+@pytest.mark.parametrize("I,J,K", [(16384, 4096, 2048), (16384, 2048, 6144), (2048, 2048, 16384)])
 def test_bf16_gemm_full_size_sampled_rows(I, J, K):
     _say(f"bf16 gemm full size {I}x{J}x{K}")
     ab = inputs.random_bits((33, I, K), (I, K), "normal")
